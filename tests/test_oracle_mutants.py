@@ -1,0 +1,64 @@
+"""Do the pins catch plausible mistakes?  (CPU only.)
+
+Each mutant is a copy of oracle/attn_oracle.c with one plausible slip planted in
+it (a dropped term, a wrong sign, a wrong index, an operand from the wrong
+tensor, a wrong causal boundary ...).  It is compiled into a temporary
+directory and every pin in oracle_pins.py is run against it; the test demands
+that at least one pin fails.  The real oracle is never modified."""
+import functools
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = [
+    ("scale_dropped", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("causal_excludes_diagonal", "causal ? p + 1 : kv_len;", "causal ? p : kv_len;"),
+    ("causal_top_left", "const int64_t p = kv_len - S_q + i;", "const int64_t p = i;"),
+    ("wrong_k_column", "(double)qi[d] * (double)kj[d]", "(double)qi[d] * (double)kj[(d + 1) % D]"),
+    ("no_max_subtraction", "s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    ("flipped_exponent", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    ("no_normalisation", "out[d] = acc / l;", "out[d] = acc;"),
+    ("drops_last_key", "causal ? p + 1 : kv_len;", "causal ? p + 1 : kv_len - 1;"),
+    ("reversed_v_column", "(double)vh[j * D + d]", "(double)vh[j * D + (D - 1 - d)]"),
+    ("row_from_list_position", "q + (bh * S_q + i) * D", "q + (bh * S_q + r) * D"),
+    ("wrong_head_for_k", "k + bh * S_kv * D, v + bh * S_kv * D", "k + (bh / 2) * S_kv * D, v + bh * S_kv * D"),
+    ("values_from_keys", "k + bh * S_kv * D, v + bh * S_kv * D", "k + bh * S_kv * D, k + bh * S_kv * D"),
+    ("max_not_taken", "if (s[j] > m) m = s[j];", "if (0) m = s[j];"),
+    ("reversed_weights", "acc += s[j] * (double)vh[j * D + d];", "acc += s[n_vis - 1 - j] * (double)vh[j * D + d];"),
+    ("normaliser_from_first_key", "l += s[j];", "l = s[0];"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(source, name, old, new):
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    mutated = source.replace(old, new)
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "m.c")
+        so = os.path.join(d, "libm.so")
+        with open(c, "w") as f:
+            f.write(mutated)
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", so, c, "-lm"], check=True)
+        lib = oracle.load(so)
+        attn = functools.partial(oracle.attention, lib=lib)
+        caught = []
+        for check in pins.ALL_CHECKS:
+            try:
+                check(attn)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(check.__name__)
+                break
+        assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,150 @@
+"""Seeded synthetic workloads for the attention forward pass.
+
+This module only draws inputs: it holds no attention arithmetic, and both the
+oracle checks and the HIP path consume what it returns.  Every tensor is
+[B, H, S, D] row-major.  Inputs are drawn as float32 N(0, sigma^2) from a
+seeded torch CPU generator (bit-reproducible on any host) and then rounded to
+the storage dtype with round-to-nearest-even; the oracle sees exactly those
+rounded values.
+
+The five workloads stand in for the hackathon benchmark the pages measure on
+(its 13 shapes and the 100k-token "case 14" are not reproduced; only the
+dimensions the pages reveal are used: B=8, S=512, d=512 on the page
+"Shape-Aware Attention", section "How we built it"; S in {128, 512, 1024, 2048}
+in its arithmetic-intensity table; batch 32, d_model 1024 and ~100k tokens on
+the page "GPU Kernel for a Transformer Layer", section "Challenges we faced").
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S_q: int
+    S_kv: int
+    D: int
+    causal: bool
+    dtypes: tuple
+    sigma: float = 1.0
+    seed: int = 0
+    outlier_frac: float = 0.0     # fraction of K rows per (b,h) scaled by outlier_mult
+    outlier_mult: float = 8.0
+    chunk: int | None = None      # query-window rows for the chunked entry point
+    sample_rows: int | None = None  # rows per (b,h) checked against the oracle
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / (self.D ** 0.5)
+
+    def flops(self) -> float:
+        """Counted work 4*B*H*S_q*S_kv*D, halved for causal."""
+        f = 4.0 * self.B * self.H * self.S_q * self.S_kv * self.D
+        return f / 2 if self.causal else f
+
+    def bytes(self, dtype: str) -> int:
+        """Algorithmic HBM bytes: Q, K, V read once, O written once."""
+        e = torch.finfo(DTYPES[dtype]).bits // 8
+        return (2 * self.S_q + 2 * self.S_kv) * self.D * e * self.B * self.H
+
+
+WORKLOADS = [
+    Workload("c1_single_head_f32", 1, 1, 128, 128, 64, False, ("f32",), seed=1,
+             note="non-causal single head, fp32, output [1,1,128,64]"),
+    Workload("c2_mha_s512", 8, 8, 512, 512, 64, False, ("f32", "f16"), seed=2,
+             note="non-causal multi-head (d_model=512), fp32 and fp16 copies of the same inputs"),
+    Workload("c3_causal_s2048", 4, 8, 2048, 2048, 64, True, ("bf16", "f16"), seed=3,
+             note="causal, key j <= query i, bf16 and fp16 separately"),
+    Workload("c4_large_batch_s1024", 32, 16, 1024, 1024, 64, False, ("bf16",), sigma=0.5, seed=4,
+             outlier_frac=0.01, note="non-causal, N(0,0.5^2), 1% of K rows per head x8"),
+    Workload("c5_long_causal_chunked", 16, 16, 98304, 98304, 64, True, ("bf16",), seed=5,
+             chunk=4096, sample_rows=256,
+             note="causal, 4096-row query windows against a K/V cache growing to 98304"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def draw_f32(shape, sigma: float, gen: torch.Generator) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, dtype=torch.float32) * sigma
+
+
+def outlier_rows(B: int, H: int, S: int, count: int, gen: torch.Generator) -> torch.Tensor:
+    """`count` distinct key-row indices per (b,h), drawn after Q, K, V."""
+    keys = torch.rand((B, H, S), generator=gen)
+    return torch.argsort(keys, dim=-1)[..., :count]
+
+
+def make_inputs(w: Workload, dtype: str, seed: int | None = None):
+    """CPU tensors (q, k, v) in the storage dtype, for workloads small enough to
+    draw on the host.  The same seed gives the same fp32 draw for every dtype,
+    so the fp16 copy is the RNE rounding of the fp32 inputs."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    q = draw_f32((w.B, w.H, w.S_q, w.D), w.sigma, g)
+    k = draw_f32((w.B, w.H, w.S_kv, w.D), w.sigma, g)
+    v = draw_f32((w.B, w.H, w.S_kv, w.D), w.sigma, g)
+    if w.outlier_frac > 0:
+        cnt = int(round(w.outlier_frac * w.S_kv))
+        idx = outlier_rows(w.B, w.H, w.S_kv, cnt, g)
+        mult = torch.ones((w.B, w.H, w.S_kv), dtype=torch.float32)
+        mult.scatter_(-1, idx, w.outlier_mult)
+        k = k * mult.unsqueeze(-1)   # power of two: exact before or after rounding
+    t = DTYPES[dtype]
+    return q.to(t), k.to(t), v.to(t)
+
+
+def make_device_inputs(w: Workload, dtype: str, device, seed: int | None = None):
+    """Draw directly on the device (for the long-context workload, 3.2 GB per
+    tensor in bf16): torch's device generator, seeded, N(0, sigma^2) in fp32
+    then rounded.  The oracle reads the resulting device bytes back."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed if seed is None else seed)
+    t = DTYPES[dtype]
+    out = []
+    for S in (w.S_q, w.S_kv, w.S_kv):
+        x = torch.empty((w.B, w.H, S, w.D), dtype=t, device=device)
+        # fill per (b,h) so no fp32 temporary of the whole tensor is needed
+        for b in range(w.B):
+            y = torch.randn((w.H, S, w.D), generator=g, device=device, dtype=torch.float32)
+            if w.sigma != 1.0:
+                y.mul_(w.sigma)
+            x[b].copy_(y)
+        out.append(x)
+    return tuple(out)
+
+
+# Rows always included in the long-context sample: both sides of the first
+# window boundaries, a late boundary and the last row.
+BOUNDARY_ROWS = (0, 1, 4095, 4096, 8191, 8192, 49151, 98303)
+
+
+def sample_rows(w: Workload, seed: int = 5005) -> torch.Tensor:
+    """[B*H, n] sorted query-row indices per (b,h): the boundary rows that fall in
+    range plus uniform draws without replacement from the rest."""
+    n = w.sample_rows or 256
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    fixed = torch.tensor([r for r in BOUNDARY_ROWS if r < w.S_q], dtype=torch.int64)
+    rows = []
+    for _ in range(w.B * w.H):
+        pool = torch.ones(w.S_q, dtype=torch.bool)
+        pool[fixed] = False
+        cand = torch.nonzero(pool).squeeze(1)
+        pick = cand[torch.randperm(cand.numel(), generator=g)[: n - fixed.numel()]]
+        rows.append(torch.sort(torch.cat([fixed, pick])).values)
+    return torch.stack(rows)
+
+
+def multi_seed_list(count: int = 40, base: int = 100):
+    """Seeds for multi-seed sweeps (40 seeds, after the page "Shape-Aware
+    Attention", section "Challenges we ran into", where one configuration
+    passed on only some seeds)."""
+    return list(range(base, base + count))
