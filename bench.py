@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one attn_fwd (or attn_fwd_chunked) call over one set of synthetic
+inputs already resident in HBM.  Inputs rotate over enough sets that the timed
+footprint exceeds the 256 MB Infinity Cache, so short workloads measure HBM,
+not the cache.  Prints ONE JSON line (rank 0, N = 1):
+
+  value        counted TFLOP/s = 4*B*H*S_q*S_kv*D (halved when causal) / time
+  ms_per_step  mean time per call over the timed region (HIP events)
+  roofline     the kernel against its binding MI355X peak (MFMA or HBM)
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload, on
+               this host's cores
+
+Default workload: multi-head non-causal S=512 (B=8, H=8, D=64) in fp32.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % of MFMA peak (ms/call) at 1 GPU, per config"
+PEAK = {  # MI355X datasheet, dense
+    "mfma_f32": 157.3, "mfma_f16": 2516.6, "mfma_bf16": 2516.6,  # TFLOP/s
+    "hbm": 8000.0,  # GB/s
+}
+ROTATE_BYTES = 1 << 30  # timed footprint target (> 256 MB Infinity Cache)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="c2_mha_s512")
+    ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def roofline_for(w, dtype, sec_per_call):
+    flops = w.flops()
+    nbytes = w.bytes(dtype)
+    t_mfma = flops / (PEAK[f"mfma_{dtype}"] * 1e12)
+    t_hbm = nbytes / (PEAK["hbm"] * 1e9)
+    if t_hbm > t_mfma:
+        ach = nbytes / sec_per_call / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK["hbm"], "unit": "GB/s",
+                "frac": round(ach / PEAK["hbm"], 4), "traffic": None}
+    ach = flops / sec_per_call / 1e12
+    pk = PEAK[f"mfma_{dtype}"]
+    return {"bound": "mfma", "achieved": round(ach, 3), "peak": pk, "unit": "TFLOP/s",
+            "frac": round(ach / pk, 4), "traffic": None}
+
+
+def cpu_baseline(w, dtype, budget_s):
+    """Time the fp64 oracle on a bounded sample of the workload's query rows."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    small = w.S_q * w.S_kv * w.B * w.H <= (1 << 27)
+    if small:
+        q, k, v = W.make_inputs(w, dtype)
+    else:  # one (b,h) head of the workload's shape
+        one = W.Workload(w.name, 1, 1, w.S_q, w.S_kv, w.D, w.causal, w.dtypes, w.sigma, w.seed,
+                         w.outlier_frac, w.outlier_mult)
+        q, k, v = W.make_inputs(one, dtype)
+    heads = q.shape[0] * q.shape[1]
+    # calibrate on a few rows, then size the sample to the time budget
+    rows_all = np.arange(w.S_q)
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    probe = np.sort(rng.choice(rows_all, size=min(w.S_q, 8), replace=False))
+    oracle.attention(q, k, v, causal=w.causal, scale=w.scale, rows=probe, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    per_row_head = dt / (len(probe) * heads)
+    n_rows = int(min(w.S_q, max(1, budget_s / (per_row_head * heads))))
+    rows = np.sort(rng.choice(rows_all, size=n_rows, replace=False)) if n_rows < w.S_q else None
+    reps = 0
+    t0 = time.perf_counter()
+    while True:  # a sample that covers the whole workload repeats until the budget is used
+        oracle.attention(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if rows is not None or el >= budget_s:
+            break
+    # counted FLOPs of the sampled rows: 4*D per visible (row, key) pair
+    shift = w.S_kv - w.S_q
+    r = rows_all if rows is None else rows
+    vis = (np.minimum(r + shift + 1, w.S_kv) if w.causal else np.full(len(r), w.S_kv)).sum()
+    flops = 4.0 * w.D * float(vis) * heads * reps
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} head(s) x {len(r)} of {w.S_q} query rows x {reps} run(s) "
+                      f"({flops / 1e9:.2f} GFLOP counted, {el:.1f} s, fp64)",
+            "seconds": round(el, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path exists in this library)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import transformer_attention_04_amd as A
+
+    w = W.BY_NAME[args.workload]
+    dtype = args.dtype or w.dtypes[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    footprint = w.bytes(dtype)
+    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
+    log(f"[bench] workload {w.name} dtype {dtype}: {footprint / 1e6:.1f} MB per set, {n_sets} sets")
+    sets = []
+    if w.S_q * w.S_kv * w.B * w.H > (1 << 32):  # long context: draw on the device
+        q, k, v = W.make_device_inputs(w, dtype, dev)
+        sets.append((q, k, v, torch.empty_like(q)))
+    else:
+        q0, k0, v0 = (x.to(dev) for x in W.make_inputs(w, dtype))
+        for i in range(n_sets):
+            if i == 0:
+                q, k, v = q0, k0, v0
+            else:  # distinct buffers, same values: the cache cannot hold them all
+                q, k, v = q0.clone(), k0.clone(), v0.clone()
+            sets.append((q, k, v, torch.empty_like(q)))
+    stream = torch.cuda.current_stream(dev)
+    chunk = w.chunk
+
+    def step(i):
+        q, k, v, o = sets[i % len(sets)]
+        if chunk:
+            A.attn_fwd_chunked(q, k, v, chunk=chunk, causal=w.causal, scale=w.scale, out=o)
+        else:
+            A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    sec = ms / 1e3
+    tflops = w.flops() / sec / 1e12
+    log(f"[bench] {ms * 1e3:.2f} us/call, {tflops:.2f} TFLOP/s, wall {wall:.3f} s")
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S_q": w.S_q, "S_kv": w.S_kv, "D_h": w.D,
+                   "causal": w.causal, "chunk": w.chunk, "rotating_sets": len(sets)},
+        "roofline": roofline_for(w, dtype, sec),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)
+    else:
+        line["cpu_baseline"] = None
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The operation is Eq. A on the page "Shape-Aware Attention" (section
+ * "Inspiration"): O = softmax(Q K^T * scale) V, optionally with a causal mask,
+ * computed with online softmax -- a running row maximum, running row sum and
+ * rescaled fp32 accumulator carried across key/value blocks, so the
+ * [B, H, S_q, S_kv] score matrix never exists (page "GPU Kernel for a
+ * Transformer Layer", section "What we learned").  Softmax statistics and the
+ * accumulator are fp32 (same section: softmax is a reduction and needs fp32).
+ * The chunked entry point processes the queries in bounded windows against a
+ * key/value cache that holds kv_len valid rows (page "Roofline", section "How
+ * we built it": bounded-memory windows against a growing key/value cache, for
+ * sequences up to ~100k tokens).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are DEVICE pointers to contiguous row-major arrays:
+ *     q, o : [B, H, S_q,  D_h]
+ *     k, v : [B, H, S_kv, D_h]
+ * all of one element type `dtype` (enum attn_dtype); o is written in that type
+ * (round-to-nearest-even from the fp32 accumulator).  Every base pointer must be
+ * 16-byte aligned; o must not overlap q, k or v.  D_h must be 64.
+ *
+ * scale multiplies q.k before the softmax; pass 1/sqrt(D_h) for Eq. A.  Any
+ * finite value is accepted (0 gives the plain mean of the visible values).
+ *
+ * Causal masking is bottom-right aligned: query row i sits at absolute
+ * position p_i = kv_len - S_q + i and sees keys j <= p_i.  With S_q == kv_len
+ * this is "key j visible to query i iff j <= i".  A causal call needs
+ * S_q <= kv_len so that every row sees at least one key.
+ *
+ * Arithmetic: Q K^T and P V run on MFMA (bf16/fp16 operands with fp32
+ * accumulation for ATTN_BF16/ATTN_F16; true fp32 MFMA for ATTN_F32).  The
+ * probabilities P are computed in fp32; on the 16-bit paths they are rounded
+ * to the input type only as the operand of the P V product (the row sum l is
+ * accumulated from the unrounded fp32 values).  No [S_q, S_kv] buffer is
+ * written anywhere.
+ *
+ * Ownership and concurrency: the caller allocates and frees every buffer.  The
+ * library allocates no device or host memory, keeps no pointer after it
+ * returns, and holds no state except a per-device "is gfx950" cache.  Work is
+ * enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream);
+ * the caller keeps the buffers alive and synchronises the stream before
+ * reading o.  Calls are thread-safe.
+ *
+ * Errors: every entry point returns ATTN_OK (0) once the work is enqueued.
+ * Otherwise it returns the first failing check below and enqueues nothing.  No
+ * entry point prints, aborts or throws.  Argument checks run before any HIP
+ * call, so they behave the same on a machine without a GPU.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_dtype {
+    ATTN_F32 = 0,   /* IEEE binary32 */
+    ATTN_F16 = 1,   /* IEEE binary16 */
+    ATTN_BF16 = 2   /* bfloat16 */
+};
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_E_NULL = 1,     /* q, k, v or o is NULL */
+    ATTN_E_SHAPE = 2,    /* B, H, S_q or S_kv < 1; D_h != 64; sizes overflow */
+    ATTN_E_DTYPE = 3,    /* dtype not an attn_dtype value */
+    ATTN_E_SCALE = 4,    /* scale is NaN or infinite */
+    ATTN_E_CAUSAL = 5,   /* causal with S_q > kv_len (a row would see no key) */
+    ATTN_E_CHUNK = 6,    /* chunk < 1, or kv_len outside [1, S_kv] */
+    ATTN_E_ALIGN = 7,    /* a base pointer is not 16-byte aligned */
+    ATTN_E_OVERLAP = 8,  /* o overlaps q, k or v */
+    ATTN_E_DEVICE = 9,   /* no current HIP device, or it is not gfx950 */
+    ATTN_E_LAUNCH = 10   /* the kernel launch reported an error */
+};
+
+/*
+ * attn_fwd -- O = softmax(Q K^T * scale [+ causal mask]) V over the whole
+ * K/V (kv_len = S_kv).  Eq. A, page "Shape-Aware Attention", section
+ * "Inspiration"; online softmax as on the page "GPU Kernel for a Transformer
+ * Layer", section "What we learned"; causal masking inside the kernel as in
+ * that page's section "How we built it".
+ *   q, k, v, o : device pointers, layouts above.
+ *   B, H       : batch size and number of heads.
+ *   S_q, S_kv  : query rows and key/value rows per (b, h).
+ *   D_h        : head dimension (must be 64).
+ *   causal     : nonzero for the causal mask.
+ *   scale      : score multiplier (finite).
+ *   dtype      : enum attn_dtype of all four tensors.
+ *   stream     : hipStream_t to enqueue on (NULL = null stream).
+ * Identical, bit for bit, to attn_fwd_chunked(..., chunk = S_q,
+ * kv_len = S_kv).
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o,
+             int B, int H, int S_q, int S_kv, int D_h,
+             int causal, float scale, int dtype, void *stream);
+
+/*
+ * attn_fwd_chunked -- the same operation with the query rows processed in
+ * windows of `chunk` rows against the first kv_len rows of a K/V cache of
+ * capacity S_kv (page "Roofline", section "How we built it"; section "What we
+ * learned": at ~100k tokens the fix is chunking/streaming).
+ *   chunk  : rows per query window, >= 1 (chunk >= S_q is a single window).
+ *   kv_len : valid K/V rows, 1 <= kv_len <= S_kv; rows >= kv_len are never read.
+ * Windows w = 0 .. ceil(S_q/chunk)-1 cover query rows [w*chunk,
+ * min(S_q, (w+1)*chunk)).  Window w reads keys [0, kv_len) when non-causal and
+ * [0, kv_len - S_q + min(S_q, (w+1)*chunk)) when causal.  All windows are
+ * enqueued as one launch, heaviest window first; memory use is O(S) for any
+ * kv_len (no workspace).  The window split changes the schedule, not the
+ * result: each output row is bit-identical to attn_fwd's on the same data.
+ * A streaming caller appends a window's K/V rows to the cache and calls with
+ * S_q = that window's rows and the grown kv_len.
+ */
+int attn_fwd_chunked(const void *q, const void *k, const void *v, void *o,
+                     int B, int H, int S_q, int S_kv, int D_h,
+                     int causal, float scale, int dtype, void *stream,
+                     int chunk, int kv_len);
+
+/*
+ * Schedule introspection (host only, no GPU needed).  attn_sched_grid writes the
+ * number of workgroups one attn_fwd_chunked call with these sizes launches
+ * (attn_fwd: chunk = S_q); attn_sched_tile writes which head (b*H + h) and
+ * which query rows [row0, row1) workgroup `block` computes.  Every (head, row)
+ * is covered by exactly one workgroup.  Both return ATTN_OK, or ATTN_E_SHAPE
+ * for sizes out of range or a NULL output pointer.
+ */
+int attn_sched_grid(int B, int H, int S_q, int chunk, int *grid);
+int attn_sched_tile(int B, int H, int S_q, int chunk, int block,
+                    int *head, int *row0, int *row1);
+
+/* Static, NUL-terminated description of an attn_status value (never NULL). */
+const char *attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

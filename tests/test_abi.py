@@ -1,0 +1,135 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every symbol the
+header declares, rejects every invalid argument with its documented code before
+touching HIP, and its launch schedule covers every (head, row) exactly once."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_04_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_fwd_chunked", "attn_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(A.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in attn.h but not exported"
+
+
+def test_status_codes_match_header():
+    src = open(HEADER).read()
+    for code, name in A.STATUS.items():
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
+        assert m and int(m.group(1)) == code, name
+
+
+def test_strerror_covers_every_code():
+    seen = set()
+    for code in A.STATUS:
+        s = A.attn_strerror(code)
+        assert s and s != A.attn_strerror(12345)
+        seen.add(s)
+    assert len(seen) == len(A.STATUS)
+    assert A.attn_strerror(12345) == "unknown attn status"
+
+
+# Fake, 16-byte aligned, non-overlapping device addresses: validation never
+# dereferences them, and every failing case returns before any HIP call.
+Q, K, V, O = 0x100000, 0x200000, 0x300000, 0x400000
+GOOD = dict(q=Q, k=K, v=V, o=O, B=2, H=3, S_q=100, S_kv=120, D=64, causal=1, scale=0.125, dtype=2,
+            chunk=64, kv_len=120)
+
+
+def call(**kw):
+    a = dict(GOOD, **kw)
+    return A.lib.attn_fwd_chunked(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["S_q"], a["S_kv"], a["D"],
+                                  a["causal"], a["scale"], a["dtype"], None, a["chunk"], a["kv_len"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1),
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(S_q=0), 2), (dict(S_kv=0), 2), (dict(D=32), 2), (dict(D=128), 2),
+    (dict(B=1 << 20, H=1 << 12), 2),                      # B*H over 2^31
+    (dict(B=1 << 14, H=1 << 14, S_q=1 << 20, S_kv=1 << 20, kv_len=1 << 20), 2),  # element count overflow
+    (dict(dtype=3), 3), (dict(dtype=-1), 3),
+    (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=float("-inf")), 4),
+    (dict(chunk=0), 6), (dict(kv_len=0), 6), (dict(kv_len=121), 6),
+    (dict(S_q=121, kv_len=120), 5), (dict(S_q=50, kv_len=40), 5),
+    (dict(q=Q + 8), 7), (dict(o=O + 4), 7), (dict(v=V + 2), 7),
+    (dict(o=Q), 8), (dict(o=K + 1024), 8), (dict(o=V - 16), 8),
+])
+def test_invalid_arguments_return_their_code(kw, code):
+    assert call(**kw) == code
+
+
+def test_valid_call_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call() == 9
+    assert A.lib.attn_fwd(Q, K, V, O, 2, 3, 100, 120, 64, 0, 0.125, 0, None) == 9
+
+
+def test_noncausal_allows_more_queries_than_keys():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call(causal=0, S_q=500, kv_len=7) == 9  # passes validation, stops at the device check
+
+
+@pytest.mark.parametrize("B,H,S_q,chunk", [
+    (1, 1, 1, 1), (1, 1, 128, 128), (1, 1, 129, 129), (2, 3, 300, 64), (2, 4, 300, 100),
+    (1, 8, 1000, 7), (4, 8, 2048, 2048), (8, 8, 512, 512), (3, 5, 777, 256), (2, 8, 5000, 4096),
+    (1, 16, 4096, 1000), (16, 1, 64, 1),
+])
+def test_schedule_covers_every_row_once(B, H, S_q, chunk):
+    grid = A.sched_grid(B, H, S_q, chunk)
+    seen = {}
+    n_win = -(-S_q // chunk)
+    for blk in range(grid):
+        h, r0, r1 = A.sched_tile(B, H, S_q, chunk, blk)
+        assert 0 <= h < B * H and 0 <= r0 < r1 <= S_q and r1 - r0 <= 128
+        assert r0 // chunk == (r1 - 1) // chunk, "tile straddles a window"
+        seen.setdefault(h, []).append((r0, r1))
+        if (B * H) % 8 == 0:
+            assert h % 8 == blk % 8, "head not on its XCD"
+    assert len(seen) == B * H
+    for h, spans in seen.items():
+        spans.sort()
+        pos = 0
+        for r0, r1 in spans:
+            assert r0 == pos
+            pos = r1
+        assert pos == S_q
+    # heaviest window first: window index never increases along each XCD's sequence
+    groups = 8 if (B * H) % 8 == 0 else 1
+    for g in range(groups):
+        wins = [A.sched_tile(B, H, S_q, chunk, b)[1] // chunk for b in range(g, grid, groups)]
+        assert wins == sorted(wins, reverse=True)
+    assert n_win == len({A.sched_tile(B, H, S_q, chunk, b)[1] // chunk for b in range(grid)})
+
+
+def test_long_context_grid_size():
+    # 98,304 rows in 4,096-row windows, 128-row tiles, 256 heads
+    assert A.sched_grid(16, 16, 98304, 4096) == 24 * 32 * 256
+    assert A.sched_grid(16, 16, 98304, 98304) == 768 * 256
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(ImportError):
+        A._load(str(tmp_path / "nope.so"))

@@ -1,0 +1,266 @@
+"""HIP path against the fp64 oracle, through the C ABI (needs an MI355X).
+
+Inputs come from the seeded generators in workloads.py; the oracle runs on the
+same rounded values.  Tolerances and the comparison rule are in parity.py."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_pins
+import workloads as W
+from parity import TOL, compare
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = W.DTYPES
+
+
+def _lib():
+    import transformer_attention_04_amd as A
+    return A
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_run(q, k, v, causal, scale=None, chunk=None, kv_len=None):
+    A = _lib()
+    qd, kd, vd = (x.to(DEV).contiguous() for x in (q, k, v))
+    if chunk is None and kv_len is None:
+        o = A.attn_fwd(qd, kd, vd, causal=causal, scale=scale)
+    else:
+        o = A.attn_fwd_chunked(qd, kd, vd, chunk=chunk or q.shape[2], kv_len=kv_len, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def check(q, k, v, dtype, causal, scale=None, chunk=None, kv_len=None, what=""):
+    o = gpu_run(q, k, v, causal, scale, chunk, kv_len)
+    ref = oracle.attention(q, k, v, causal=causal, scale=scale, kv_len=kv_len)
+    return compare(o.float().cpu().numpy(), ref, dtype, what)
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,dtype", [
+    ("c1_single_head_f32", "f32"),
+    ("c2_mha_s512", "f32"),
+    ("c2_mha_s512", "f16"),
+    ("c3_causal_s2048", "bf16"),
+    ("c3_causal_s2048", "f16"),
+])
+def test_workload_full(name, dtype):
+    w = W.BY_NAME[name]
+    say(f"[parity] {name} {dtype}")
+    q, k, v = W.make_inputs(w, dtype)
+    err, ratio = check(q, k, v, dtype, w.causal, w.scale, what=f"{name}/{dtype}")
+    say(f"[parity] {name} {dtype}: max|err| {err:.3e}, worst err/bound {ratio:.3f}")
+
+
+def test_workload_c4_sampled():
+    """Full-size launch; the oracle checks 6 whole heads and 48 rows of every head."""
+    w = W.BY_NAME["c4_large_batch_s1024"]
+    q, k, v = W.make_inputs(w, "bf16")
+    o = gpu_run(q, k, v, False, w.scale).float().cpu().numpy()
+    heads = [(0, 0), (0, 15), (7, 3), (16, 8), (31, 0), (31, 15)]
+    for b, h in heads:
+        ref = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale=w.scale)
+        compare(o[b:b + 1, h:h + 1], ref, "bf16", f"c4 head {(b, h)}")
+    rows = np.random.default_rng(44).choice(w.S_q, size=48, replace=False)
+    ref = oracle.attention(q, k, v, scale=w.scale, rows=rows)
+    err, ratio = compare(o[:, :, rows], ref, "bf16", "c4 sampled rows")
+    say(f"[parity] c4 bf16 sampled: max|err| {err:.3e}, worst err/bound {ratio:.3f}")
+
+
+# ---------------------------------------------------------------------------
+# ragged, tiny and rectangular shapes
+# ---------------------------------------------------------------------------
+EDGE = [  # (B, H, S_q, S_kv, causal)
+    (1, 1, 1, 1, False), (1, 1, 1, 1, True), (1, 1, 2, 3, False), (1, 1, 3, 5, True),
+    (1, 2, 5, 17, True), (2, 1, 17, 17, True), (1, 1, 63, 64, False), (1, 1, 64, 64, True),
+    (1, 1, 65, 65, True), (1, 3, 127, 129, False), (1, 1, 129, 129, True), (2, 2, 200, 200, True),
+    (1, 1, 200, 63, False), (1, 1, 1, 200, False), (1, 1, 1, 200, True), (1, 2, 33, 300, True),
+    (2, 4, 257, 257, True), (1, 8, 130, 70, False), (3, 1, 300, 301, True), (1, 1, 512, 1000, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_edge_shapes(dtype):
+    worst = 0.0
+    for n, (B, H, S_q, S_kv, causal) in enumerate(EDGE):
+        w = W.Workload("edge", B, H, S_q, S_kv, 64, causal, (dtype,), seed=900 + n)
+        q, k, v = W.make_inputs(w, dtype)
+        _, r = check(q, k, v, dtype, causal, what=f"edge {(B, H, S_q, S_kv, causal)} {dtype}")
+        worst = max(worst, r)
+    say(f"[parity] edge shapes {dtype}: worst err/bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 1e-3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scales(dtype, scale):
+    w = W.Workload("scale", 1, 2, 150, 170, 64, True, (dtype,), seed=77)
+    q, k, v = W.make_inputs(w, dtype)
+    check(q, k, v, dtype, True, scale=scale, what=f"scale {scale}")
+    check(q, k, v, dtype, False, scale=scale, what=f"scale {scale} noncausal")
+
+
+# ---------------------------------------------------------------------------
+# the chunked entry point
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_partial_cache_vs_oracle(dtype):
+    """Query window at the end of a K/V cache whose first kv_len rows are valid."""
+    w = W.Workload("cache", 2, 2, 96, 700, 64, True, (dtype,), seed=31)
+    q, k, v = W.make_inputs(w, dtype)
+    for kv_len in (96, 97, 500, 640, 700):
+        for chunk in (32, 96, 1000):
+            check(q, k, v, dtype, True, chunk=chunk, kv_len=kv_len, what=f"kv_len {kv_len} chunk {chunk}")
+    check(q, k, v, dtype, False, chunk=50, kv_len=333, what="non-causal kv_len 333")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_equals_unchunked_bitwise(dtype):
+    w = W.Workload("chunk", 2, 4, 1500, 1500, 64, True, (dtype,), seed=12)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, dtype))
+    A = _lib()
+    for causal in (True, False):
+        ref = A.attn_fwd(q, k, v, causal=causal)
+        for chunk in (1, 7, 100, 128, 256, 512, 1499, 4096):
+            o = A.attn_fwd_chunked(q, k, v, chunk=chunk, causal=causal)
+            assert torch.equal(o, ref), f"chunk {chunk} causal {causal} differs"
+
+
+def test_streaming_windows_equal_single_call():
+    """Window-by-window calls with a growing kv_len give the single call's rows."""
+    A = _lib()
+    w = W.Workload("stream", 1, 8, 3000, 3000, 64, True, ("bf16",), seed=13)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, "bf16"))
+    full = A.attn_fwd_chunked(q, k, v, chunk=512, causal=True)
+    out = torch.empty_like(q)
+    for start in range(0, 3000, 512):
+        stop = min(3000, start + 512)
+        qw = q[:, :, start:stop].contiguous()
+        ow = A.attn_fwd_chunked(qw, k, v, chunk=512, kv_len=stop, causal=True)
+        out[:, :, start:stop] = ow
+    torch.cuda.synchronize()
+    assert torch.equal(out, full)
+
+
+# ---------------------------------------------------------------------------
+# closed forms and invariants on the device
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_one_hot_selects_value_rows_exactly(dtype):
+    for causal in (False, True):
+        q, k, v, target = oracle_pins.one_hot_inputs(160, 300, 64, causal, seed=5)
+        t = TD[dtype]
+        q, k, v = (torch.from_numpy(x).to(t) for x in (q, k, v))
+        o = gpu_run(q, k, v, causal, 0.125).cpu()
+        for i, tt in enumerate(target):
+            if tt >= 0:
+                assert torch.equal(o[0, 0, i], v[0, 0, tt]), f"row {i} causal {causal}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_single_visible_key(dtype):
+    """Causal row 0 (S_q = S_kv) and kv_len = 1 return value row 0: exactly for
+    16-bit outputs, within 2 ulp for fp32 (the probability of the only key is
+    exp2 of a rounding residual, ~1 +- 2^-23)."""
+    w = W.Workload("one", 2, 3, 140, 140, 64, True, (dtype,), seed=14)
+    q, k, v = W.make_inputs(w, dtype)
+    o = gpu_run(q, k, v, True).cpu()
+    o1 = gpu_run(q, k, v, False, chunk=140, kv_len=1).cpu()
+    want = v[:, :, 0]
+    if dtype == "f32":
+        for got in (o[:, :, 0], o1[:, :, 0], o1[:, :, 77]):
+            assert torch.allclose(got, want, rtol=2.5e-7, atol=0)
+    else:
+        assert torch.equal(o[:, :, 0], want)
+        assert torch.equal(o1[:, :, 0], want) and torch.equal(o1[:, :, 77], want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_value_scaling_is_exact(dtype):
+    w = W.Workload("vs", 1, 2, 200, 333, 64, True, (dtype,), seed=15)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, dtype))
+    A = _lib()
+    a = A.attn_fwd(q, k, v, causal=True)
+    b = A.attn_fwd(q, k, v * 8, causal=True)
+    assert torch.equal(b, a * 8)
+
+
+def test_zero_queries_give_prefix_means():
+    w = W.Workload("zq", 1, 2, 130, 130, 64, True, ("bf16",), seed=16)
+    q, k, v = W.make_inputs(w, "bf16")
+    q = torch.zeros_like(q)
+    check(q, k, v, "bf16", True, what="Q=0 causal")
+    check(q, k, v, "bf16", False, what="Q=0")
+
+
+def test_query_permutation_permutes_rows():
+    w = W.Workload("perm", 1, 2, 256, 256, 64, False, ("bf16",), seed=17)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, "bf16"))
+    A = _lib()
+    perm = torch.randperm(256, generator=torch.Generator().manual_seed(3)).to(DEV)
+    a = A.attn_fwd(q, k, v)
+    b = A.attn_fwd(q[:, :, perm].contiguous(), k, v)
+    assert torch.equal(b, a[:, :, perm])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deterministic_repeats(dtype):
+    w = W.Workload("det", 4, 8, 1024, 1024, 64, True, (dtype,), seed=18)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, dtype))
+    A = _lib()
+    first = A.attn_fwd(q, k, v, causal=True)
+    for _ in range(20):
+        assert torch.equal(A.attn_fwd(q, k, v, causal=True), first)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_output_guard_bands_untouched(dtype):
+    A = _lib()
+    B, H, S_q, S_kv = 2, 3, 333, 400
+    w = W.Workload("guard", B, H, S_q, S_kv, 64, True, (dtype,), seed=19)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, dtype))
+    n = B * H * S_q * 64
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 7.0, dtype=TD[dtype], device=DEV)
+    o = buf[pad:pad + n].view(B, H, S_q, 64)
+    A.attn_fwd_chunked(q, k, v, chunk=100, kv_len=S_kv, causal=True, out=o)
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == 7).all()) and bool((buf[pad + n:] == 7).all())
+    ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=True)
+    compare(o.float().cpu().numpy(), ref, dtype, "guard")
+
+
+def test_multi_seed_sweep():
+    """40 seeds on the single-head fp32 workload and a small causal bf16 shape."""
+    w1 = W.BY_NAME["c1_single_head_f32"]
+    w2 = W.Workload("seeds", 1, 4, 256, 256, 64, True, ("bf16",))
+    for s in W.multi_seed_list():
+        q, k, v = W.make_inputs(w1, "f32", seed=s)
+        check(q, k, v, "f32", False, what=f"c1 seed {s}")
+        q, k, v = W.make_inputs(w2, "bf16", seed=s)
+        check(q, k, v, "bf16", True, what=f"causal seed {s}")
+
+
+def test_binding_rejects_bad_tensors():
+    A = _lib()
+    q = torch.zeros(1, 1, 8, 64, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        A.attn_fwd(q, q.half(), q)
+    with pytest.raises(ValueError):
+        A.attn_fwd(q, q[:, :, :, :32].contiguous(), q)
+    with pytest.raises(A.AttnError) as e:
+        A.attn_fwd(q, q[:, :, :4].contiguous(), q[:, :, :4].contiguous(), causal=True)
+    assert e.value.status == 5
+    with pytest.raises(A.AttnError):
+        A.attn_fwd(torch.zeros(1, 1, 8, 32, device=DEV, dtype=torch.bfloat16),
+                   torch.zeros(1, 1, 8, 32, device=DEV, dtype=torch.bfloat16),
+                   torch.zeros(1, 1, 8, 32, device=DEV, dtype=torch.bfloat16))

@@ -1,0 +1,151 @@
+"""Python binding of the MI355X fused attention forward library (libattn.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/attn.h.  torch supplies device
+memory and the current stream.  There is no fallback: if the library is not
+built, importing this package raises.
+
+    attn_fwd(q, k, v, causal=False, scale=None)            -> o
+    attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o
+    attn_strerror(status)                                    -> str
+
+q: [B, H, S_q, 64]; k, v: [B, H, S_kv, 64]; all contiguous, same dtype
+(float32, float16 or bfloat16) and same CUDA (HIP) device.  scale=None means
+1/sqrt(64) (Eq. A, page "Shape-Aware Attention", section "Inspiration").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_DTYPE", 4: "ATTN_E_SCALE",
+    5: "ATTN_E_CAUSAL", 6: "ATTN_E_CHUNK", 7: "ATTN_E_ALIGN", 8: "ATTN_E_OVERLAP",
+    9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH",
+}
+EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run transformer_attention_04_amd/build.py "
+                          "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, i, i]
+    lib.attn_fwd_chunked.restype = i
+    lib.attn_strerror.argtypes = [i]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_sched_grid.argtypes = [i, i, i, i, ctypes.POINTER(i)]
+    lib.attn_sched_grid.restype = i
+    lib.attn_sched_tile.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.attn_sched_tile.restype = i
+    return lib
+
+
+lib = _load()
+
+
+def attn_strerror(status: int) -> str:
+    return lib.attn_strerror(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, D], got {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, S_q, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, H, S_q, k.shape[2], D
+
+
+def _stream_ptr(device, stream):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd_chunked(q, k, v, chunk: int, kv_len: int | None = None, causal: bool = False,
+                     scale: float | None = None, out=None, stream=None):
+    """Chunked/streaming forward: query windows of `chunk` rows against the first
+    kv_len rows of the K/V cache (see attn_fwd_chunked in include/attn.h)."""
+    import torch
+    B, H, S_q, S_kv, D = _check(q, k, v)
+    if kv_len is None:
+        kv_len = S_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
+                                  _dtype_code(q), _stream_ptr(q.device, stream), int(chunk), int(kv_len))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return o
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, stream=None):
+    """O = softmax(Q K^T * scale [+ causal mask]) V (see attn_fwd in include/attn.h)."""
+    import torch
+    B, H, S_q, S_kv, D = _check(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
+                          _dtype_code(q), _stream_ptr(q.device, stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return o
+
+
+def sched_grid(B: int, H: int, S_q: int, chunk: int) -> int:
+    g = ctypes.c_int()
+    st = lib.attn_sched_grid(B, H, S_q, chunk, ctypes.byref(g))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return g.value
+
+
+def sched_tile(B: int, H: int, S_q: int, chunk: int, block: int):
+    h, r0, r1 = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = lib.attn_sched_tile(B, H, S_q, chunk, block, ctypes.byref(h), ctypes.byref(r0), ctypes.byref(r1))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return h.value, r0.value, r1.value

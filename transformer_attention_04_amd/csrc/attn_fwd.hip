@@ -1,0 +1,799 @@
+// attn_fwd.hip -- fused attention forward for AMD Instinct MI355X (gfx950).
+//
+// O = softmax(Q K^T * scale [+ causal mask]) V  (Eq. A, page "Shape-Aware
+// Attention", section "Inspiration") with online softmax: each query row keeps
+// a running maximum m, a running sum l and an fp32 accumulator across key/value
+// blocks, rescaling when the maximum grows (page "GPU Kernel for a Transformer
+// Layer", section "What we learned"), so no [S_q, S_kv] score matrix exists.
+// Causal masking is applied inside the kernel, only on the blocks that need it,
+// and key blocks wholly above the diagonal are never loaded (same page, section
+// "How we built it", for the causal kernel).  The chunked entry point enqueues
+// query windows against the valid prefix of a K/V cache (page "Roofline",
+// section "How we built it").
+//
+// Work decomposition (both element types)
+//   workgroup = 4 wavefronts x 32 query rows = BM = 128 rows of one (b, h);
+//   per iteration the workgroup stages BN = 64 keys of K and V in LDS
+//   (double-buffered, 128-bit coalesced global loads issued one tile ahead);
+//   each wave computes S^T = K Q^T on MFMA so that a lane owns ONE query row
+//   (lane % 32) and 16 keys per 32-key block: the row max and row sum are
+//   in-lane plus one exchange between the two half-waves (v_permlane32_swap);
+//   P^T feeds the B operand of O^T = V^T P^T straight from registers; the O^T
+//   accumulator is also per-lane-row, so rescaling by exp2(m_old - m_new) is a
+//   per-lane multiply.
+//   16-bit inputs: v_mfma_f32_32x32x16_{bf16,f16}; V^T operands come from
+//   ds_read_b64_tr_b16 on the natural [key][d] LDS tile.
+//   fp32 inputs: v_mfma_f32_32x32x2f32 (true fp32; gfx950 has no xf32 MFMA).
+//
+// Softmax numerics: scores, m, l and the accumulator are fp32.  exp(x) is
+// evaluated as exp2(x * log2 e) with log2 e folded into the score scale (one
+// FMA per score).  The row maximum used as the exponent offset is only raised
+// when a new block exceeds it by more than 2^8 ("lazy" rescaling); this keeps
+// every probability <= 256, changes nothing in exact arithmetic (the offset
+// cancels between numerator and denominator), and skips the accumulator
+// rescale on most blocks.  Probabilities are rounded to bf16/fp16 only as the
+// MFMA operand of the P V product; l sums the fp32 values.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int HEAD_DIM = 64;
+constexpr int BM = 128;        // query rows per workgroup
+constexpr int BN = 64;         // keys per iteration
+constexpr int NTHREADS = 256;  // 4 wavefronts of 64
+constexpr float LAZY_TH = 8.0f;  // log2 headroom before the offset is raised
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// ---------------------------------------------------------------------------
+// Schedule: blockIdx.x -> (head, query rows [row0, row1)).
+// Windows are enqueued heaviest first (the last window sees the longest key
+// prefix when causal); inside a window tiles run from the diagonal end
+// backwards.  When B*H is a multiple of 8, head h only runs on XCD h % 8
+// (workgroups are dealt to the 8 XCDs round-robin by id), so the query tiles
+// of one head share that XCD's L2 for their common K/V prefix.
+// ---------------------------------------------------------------------------
+struct Sched {
+  int S_q;
+  int chunk;   // rows per window
+  int n_win;   // windows
+  int tf;      // tiles per full window
+  int tl;      // tiles in the last window
+  int heads;   // heads enumerated per decode group
+  int groups;  // 8 (XCD-grouped) or 1
+};
+
+__host__ __device__ inline void decode_tile(const Sched& s, int b, int& head, int& row0, int& row1) {
+  int grp = 0, L = b;
+  if (s.groups == 8) {
+    grp = b & 7;
+    L = b >> 3;
+  }
+  const int last = s.n_win - 1;
+  const int n_last = s.heads * s.tl;
+  int w, j, t;
+  if (L < n_last) {
+    w = last;
+    j = L / s.tl;
+    t = s.tl - 1 - (L - j * s.tl);
+  } else {
+    const int L2 = L - n_last;
+    const int per = s.heads * s.tf;
+    const int wi = L2 / per;
+    const int rem = L2 - wi * per;
+    w = last - 1 - wi;
+    j = rem / s.tf;
+    t = s.tf - 1 - (rem - j * s.tf);
+  }
+  head = j * s.groups + grp;
+  const int wstart = w * s.chunk;
+  const int wend = min(s.S_q, wstart + s.chunk);
+  row0 = wstart + t * BM;
+  row1 = min(wend, row0 + BM);
+}
+
+template <typename T>
+struct Params {
+  const T* q;
+  const T* k;
+  const T* v;
+  T* o;
+  int64_t q_head_stride;   // S_q * 64 elements
+  int64_t kv_head_stride;  // S_kv * 64 elements
+  int S_q;
+  int kv_len;
+  float c;          // |scale| * log2(e)
+  unsigned q_flip;  // XOR mask on Q's 32-bit words: sign flip for negative scale
+  Sched s;
+};
+
+__device__ __forceinline__ float other_half(float x) {
+  // value held by lane l ^ 32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(threadIdx.x & 32 ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// 16-bit element types
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Half16;
+
+template <>
+struct Half16<__bf16> {
+  typedef bf16x8 vec8;
+  __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ unsigned pack2(float x, float y) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
+  }
+};
+
+template <>
+struct Half16<_Float16> {
+  typedef f16x8 vec8;
+  __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ unsigned pack2(float x, float y) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, f16x2));
+  }
+};
+
+// LDS tile of 64 rows x 128 bytes (64 16-bit values) = 8 KB.  16-byte chunks
+// are XOR-swizzled per row to keep the MFMA operand reads conflict-free.
+// K is read as one 16-byte chunk per lane, 16 consecutive rows per access.
+__device__ __forceinline__ int k16_off(int row, int c16) {
+  return row * 128 + ((c16 ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
+}
+// V is read with ds_read_b64_tr_b16: per 16-lane group, 4 consecutive rows x
+// 2 adjacent chunks; shifting the chunk pair by 2*(row & 3) spreads them over 8
+// distinct chunks.
+__device__ __forceinline__ int v16_off(int row, int c16) {
+  return row * 128 + ((c16 ^ ((row & 3) << 1)) << 4);
+}
+
+template <typename T, bool CAUSAL>
+__global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
+  typedef Half16<T> H;
+  typedef typename H::vec8 vec8;
+  __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];  // [stage][K,V]
+
+  int head, row0, row1;
+  decode_tile(p.s, blockIdx.x, head, row0, row1);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;  // query column of the S^T / O^T tiles
+  const int hf = lane >> 5;  // half-wave
+
+  const T* qh = p.q + (int64_t)head * p.q_head_stride;
+  const T* kh = p.k + (int64_t)head * p.kv_head_stride;
+  const T* vh = p.v + (int64_t)head * p.kv_head_stride;
+  T* oh = p.o + (int64_t)head * p.q_head_stride;
+
+  const int kv_len = p.kv_len;
+  const int shift = kv_len - p.S_q;  // absolute position of query row r is r + shift
+  const int kv_end = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  // This wave's query rows and their positions.
+  const int wrow0 = row0 + wave * 32;
+  const int qrow = wrow0 + c;
+  const bool wave_live = wrow0 < row1;
+  const int wlast = min(wrow0 + 31, row1 - 1);  // last valid row of the wave
+  const int pos = qrow + shift;
+  const int pos_first = wrow0 + shift;
+  const int pos_last = wlast + shift;
+
+  // Q^T operand: lane holds Q[qrow][32*hf + 8*t .. +7] for k-step t.
+  vec8 qop[4];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * HEAD_DIM + 32 * hf);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qrow < row1) x = src[t];
+      x ^= p.q_flip;
+      qop[t] = __builtin_bit_cast(vec8, x);
+    }
+  }
+
+  // Global -> register prefetch of one K/V tile: thread owns chunks tid and
+  // tid + 256 of the 512 16-byte chunks of each 8 KB tile.
+  const int ld_row = tid >> 3;  // 0..31 (+32 for the second chunk)
+  const int ld_c16 = tid & 7;
+  u32x4 pk[2], pv[2];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = kv0 + ld_row + 32 * i;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (row < kv_len) {
+        pk[i] = *reinterpret_cast<const u32x4*>(kh + (int64_t)row * HEAD_DIM + ld_c16 * 8);
+        pv[i] = *reinterpret_cast<const u32x4*>(vh + (int64_t)row * HEAD_DIM + ld_c16 * 8);
+      } else {
+        pk[i] = z;
+        pv[i] = z;
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = ld_row + 32 * i;
+      *reinterpret_cast<u32x4*>(&smem[stage][0][k16_off(row, ld_c16)]) = pk[i];
+      *reinterpret_cast<u32x4*>(&smem[stage][1][v16_off(row, ld_c16)]) = pv[i];
+    }
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[0][r] = 0.f;
+    acc[1][r] = 0.f;
+  }
+  float m = -INFINITY;  // exponent offset (log2 units), per row
+  float l = 0.f;        // this lane's share of the row sum
+
+  const float cc = p.c;
+
+  if (n_tiles > 0) load_tile(0);
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it & 1;
+    const int kv0 = it * BN;
+    store_tile(stage);
+    if (it + 1 < n_tiles) load_tile(kv0 + BN);
+    __syncthreads();
+
+    // Which 32-key blocks of this tile can any row of this wave see?
+    bool blk[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int first_key = kv0 + 32 * kb;
+      blk[kb] = wave_live && first_key < kv_len && (!CAUSAL || first_key <= pos_last);
+    }
+    if (!blk[0]) continue;  // blk[1] implies blk[0]
+
+    const char* ks = smem[stage][0];
+    const char* vs = smem[stage][1];
+
+    // S^T = K Q^T for the two 32-key blocks.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && !blk[1]) continue;
+        const vec8 a = *reinterpret_cast<const vec8*>(ks + k16_off(32 * kb + c, 4 * hf + t));
+        s[kb] = H::mfma(a, qop[t], s[kb]);
+      }
+    }
+
+    // Masking: only blocks that cross the diagonal or the end of the cache.
+    bool masked = false;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int first_key = kv0 + 32 * kb;
+      const bool need = !blk[kb] || first_key + 31 >= kv_len || (CAUSAL && first_key + 31 > pos_first);
+      if (need) {
+        masked = true;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = first_key + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = blk[kb] && key < kv_len && (!CAUSAL || key <= pos);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
+      }
+    }
+
+    // Row maximum of the raw scores over the 64 keys.
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_halves(mx);
+    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * cc;
+
+    // Lazy offset update: raise m only when the block exceeds it by > 2^8.
+    const bool raise = mxc > m + LAZY_TH;
+    if (__any(raise)) {
+      const float m_new = raise ? mxc : m;
+      const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf, 1 if unchanged
+      l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[0][r] *= alpha;
+        acc[1][r] *= alpha;
+      }
+      m = m_new;
+    }
+    const float moff = (m == -INFINITY) ? 0.f : m;
+
+    // P = exp2(s * c - m), row sum, bf16/fp16 pack for the P V operand.
+    unsigned pp[2][8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
+        float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
+        if (masked) {
+          e0 = (s[kb][r] == -INFINITY) ? 0.f : e0;
+          e1 = (s[kb][r + 1] == -INFINITY) ? 0.f : e1;
+        }
+        lsum += e0 + e1;
+        pp[kb][r >> 1] = H::pack2(e0, e1);
+      }
+    }
+    l += lsum;
+
+    // O^T += V^T P^T.  B operand (k-slot 8*hf + e) is P[kb][8u + e]; the A
+    // operand lane (d, hf) needs V[32kb + 16u + 8(e/4) + 4hf + e%4][d], read
+    // transposed from the [key][d] tile: source lane s of each 16-lane group
+    // reads row kbase + s/4, columns d0 + 4(s%4) .. +3.
+    const int g = lane >> 4;  // 16-lane group
+    const int sl = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && !blk[1]) continue;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 bw = {pp[kb][4 * u], pp[kb][4 * u + 1], pp[kb][4 * u + 2], pp[kb][4 * u + 3]};
+        const vec8 b = __builtin_bit_cast(vec8, bw);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+          const int c16 = d0 >> 3;
+          const int half = (d0 >> 2) & 1;
+          i16x4 lo, hi;
+          {
+            const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
+          }
+          {
+            const int row = 32 * kb + 16 * u + 8 + 4 * (g >> 1) + (sl >> 2);
+            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
+          }
+          u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          acc[dt] = H::mfma(__builtin_bit_cast(vec8, aw), b, acc[dt]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: O = acc / l, RNE to T, rows of this wave that exist.
+  const float lt = l + other_half(l);
+  const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
+  if (qrow < row1) {
+    T* orow = oh + (int64_t)qrow * HEAD_DIM;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * dt + 8 * gq + 4 * hf;
+        u32x2 w;
+        w[0] = H::pack2(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv);
+        w[1] = H::pack2(acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32
+// ---------------------------------------------------------------------------
+// LDS tile of 64 rows x 256 bytes (64 floats) = 16 KB, 16 chunks per row.
+__device__ __forceinline__ int k32_off(int row, int c16) {
+  return row * 256 + ((c16 ^ (row & 15)) << 4);
+}
+// V^T reads take one float per lane: 32 consecutive columns from row R (lanes
+// 0-31) and row R+4 (lanes 32-63); the extra bit keeps the two rows' chunks in
+// different halves of the row.
+__device__ __forceinline__ int v32_off(int row, int col) {
+  const int x = (row & 15) ^ (((row >> 2) & 1) << 3);
+  return row * 256 + (((col >> 2) ^ x) << 4) + ((col & 3) << 2);
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k32(Params<float> p) {
+  __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 256];  // [stage][K,V]
+
+  int head, row0, row1;
+  decode_tile(p.s, blockIdx.x, head, row0, row1);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int hf = lane >> 5;
+
+  const float* qh = p.q + (int64_t)head * p.q_head_stride;
+  const float* kh = p.k + (int64_t)head * p.kv_head_stride;
+  const float* vh = p.v + (int64_t)head * p.kv_head_stride;
+  float* oh = p.o + (int64_t)head * p.q_head_stride;
+
+  const int kv_len = p.kv_len;
+  const int shift = kv_len - p.S_q;
+  const int kv_end = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  const int wrow0 = row0 + wave * 32;
+  const int qrow = wrow0 + c;
+  const bool wave_live = wrow0 < row1;
+  const int wlast = min(wrow0 + 31, row1 - 1);
+  const int pos = qrow + shift;
+  const int pos_first = wrow0 + shift;
+  const int pos_last = wlast + shift;
+
+  // Q^T operand: k-step t uses d = 32*hf + t, so the lane holds Q[qrow][32hf .. 32hf+31].
+  float qv[32];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * HEAD_DIM + 32 * hf);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qrow < row1) x = src[j];
+      x ^= p.q_flip;
+      qv[4 * j + 0] = __uint_as_float(x[0]);
+      qv[4 * j + 1] = __uint_as_float(x[1]);
+      qv[4 * j + 2] = __uint_as_float(x[2]);
+      qv[4 * j + 3] = __uint_as_float(x[3]);
+    }
+  }
+
+  // thread owns chunks tid + 256 i (i < 4) of the 1024 16-byte chunks of a tile
+  const int ld_row = tid >> 4;  // 0..15 (+16 i)
+  const int ld_c16 = tid & 15;
+  u32x4 pk[4], pv[4];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = kv0 + ld_row + 16 * i;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (row < kv_len) {
+        pk[i] = *reinterpret_cast<const u32x4*>(kh + (int64_t)row * HEAD_DIM + ld_c16 * 4);
+        pv[i] = *reinterpret_cast<const u32x4*>(vh + (int64_t)row * HEAD_DIM + ld_c16 * 4);
+      } else {
+        pk[i] = z;
+        pv[i] = z;
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ld_row + 16 * i;
+      *reinterpret_cast<u32x4*>(&smem[stage][0][k32_off(row, ld_c16)]) = pk[i];
+      *reinterpret_cast<u32x4*>(&smem[stage][1][v32_off(row, 4 * ld_c16)]) = pv[i];
+    }
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[0][r] = 0.f;
+    acc[1][r] = 0.f;
+  }
+  float m = -INFINITY;
+  float l = 0.f;
+  const float cc = p.c;
+
+  if (n_tiles > 0) load_tile(0);
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it & 1;
+    const int kv0 = it * BN;
+    store_tile(stage);
+    if (it + 1 < n_tiles) load_tile(kv0 + BN);
+    __syncthreads();
+
+    bool blk[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int first_key = kv0 + 32 * kb;
+      blk[kb] = wave_live && first_key < kv_len && (!CAUSAL || first_key <= pos_last);
+    }
+    if (!blk[0]) continue;
+
+    const char* ks = smem[stage][0];
+    const char* vs = smem[stage][1];
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && !blk[1]) continue;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + k32_off(32 * kb + c, 8 * hf + j));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), qv[4 * j + e], s[kb], 0, 0, 0);
+      }
+    }
+
+    bool masked = false;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int first_key = kv0 + 32 * kb;
+      const bool need = !blk[kb] || first_key + 31 >= kv_len || (CAUSAL && first_key + 31 > pos_first);
+      if (need) {
+        masked = true;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = first_key + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = blk[kb] && key < kv_len && (!CAUSAL || key <= pos);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
+      }
+    }
+
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_halves(mx);
+    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * cc;
+
+    const bool raise = mxc > m + LAZY_TH;
+    if (__any(raise)) {
+      const float m_new = raise ? mxc : m;
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[0][r] *= alpha;
+        acc[1][r] *= alpha;
+      }
+      m = m_new;
+    }
+    const float moff = (m == -INFINITY) ? 0.f : m;
+
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
+        if (masked) e = (s[kb][r] == -INFINITY) ? 0.f : e;
+        lsum += e;
+        s[kb][r] = e;
+      }
+    }
+    l += lsum;
+
+    // O^T += V^T P^T, one key pair per MFMA: k-slot hf of step r is key
+    // 32kb + 8(r/4) + 4hf + r%4, whose probability is this lane's s[kb][r].
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && !blk[1]) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const float a = *reinterpret_cast<const float*>(vs + v32_off(key, 32 * dt + c));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float lt = l + other_half(l);
+  const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
+  if (qrow < row1) {
+    float* orow = oh + (int64_t)qrow * HEAD_DIM;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * dt + 8 * gq + 4 * hf;
+        u32x4 w;
+        w[0] = __float_as_uint(acc[dt][4 * gq] * inv);
+        w[1] = __float_as_uint(acc[dt][4 * gq + 1] * inv);
+        w[2] = __float_as_uint(acc[dt][4 * gq + 2] * inv);
+        w[3] = __float_as_uint(acc[dt][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x4*>(orow + d) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+std::atomic<int> g_arch_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_E_DEVICE;
+  if (dev < 64) {
+    const int s = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (s == 1) return ATTN_OK;
+    if (s == 2) return ATTN_E_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_E_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? ATTN_OK : ATTN_E_DEVICE;
+}
+
+bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uint64_t pa = (uint64_t)(uintptr_t)a, pb = (uint64_t)(uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int validate(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
+             int D_h, int causal, float scale, int dtype, int chunk, int kv_len) {
+  if (!q || !k || !v || !o) return ATTN_E_NULL;
+  if (B < 1 || H < 1 || S_q < 1 || S_kv < 1 || D_h != HEAD_DIM) return ATTN_E_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  if (!std::isfinite(scale)) return ATTN_E_SCALE;
+  if (chunk < 1 || kv_len < 1 || kv_len > S_kv) return ATTN_E_CHUNK;
+  if (causal && S_q > kv_len) return ATTN_E_CAUSAL;
+  // sizes: elements and bytes fit in int64; the grid fits in 2^31 - 1
+  const int64_t bh = (int64_t)B * H;
+  if (bh > (int64_t)INT32_MAX) return ATTN_E_SHAPE;
+  const int64_t esz = dtype == ATTN_F32 ? 4 : 2;
+  const int64_t lim = INT64_MAX / (HEAD_DIM * esz);
+  if ((int64_t)S_q > lim / bh || (int64_t)S_kv > lim / bh) return ATTN_E_SHAPE;
+  const int64_t n_win = ((int64_t)S_q + chunk - 1) / chunk;
+  const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + BM - 1) / BM);
+  if (tiles * bh > (int64_t)INT32_MAX) return ATTN_E_SHAPE;
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
+  if (mis) return ATTN_E_ALIGN;
+  const uint64_t nq = (uint64_t)bh * S_q * HEAD_DIM * esz;
+  const uint64_t nkv = (uint64_t)bh * S_kv * HEAD_DIM * esz;
+  if (ranges_overlap(o, nq, q, nq) || ranges_overlap(o, nq, k, nkv) || ranges_overlap(o, nq, v, nkv))
+    return ATTN_E_OVERLAP;
+  return ATTN_OK;
+}
+
+Sched make_sched(int B, int H, int S_q, int chunk) {
+  Sched s;
+  s.S_q = S_q;
+  s.chunk = std::min(chunk, S_q);
+  s.n_win = (S_q + s.chunk - 1) / s.chunk;
+  s.tf = (s.chunk + BM - 1) / BM;
+  const int last_rows = S_q - (s.n_win - 1) * s.chunk;
+  s.tl = (last_rows + BM - 1) / BM;
+  const int bh = B * H;
+  s.groups = (bh % 8 == 0) ? 8 : 1;
+  s.heads = bh / s.groups;
+  return s;
+}
+
+template <typename T>
+int launch_typed(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
+                 int causal, float scale, hipStream_t stream, int chunk, int kv_len) {
+  Params<T> p;
+  p.q = static_cast<const T*>(q);
+  p.k = static_cast<const T*>(k);
+  p.v = static_cast<const T*>(v);
+  p.o = static_cast<T*>(o);
+  p.q_head_stride = (int64_t)S_q * HEAD_DIM;
+  p.kv_head_stride = (int64_t)S_kv * HEAD_DIM;
+  p.S_q = S_q;
+  p.kv_len = kv_len;
+  p.c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+  p.q_flip = (scale < 0.f) ? (sizeof(T) == 4 ? 0x80000000u : 0x80008000u) : 0u;
+  p.s = make_sched(B, H, S_q, chunk);
+  const int grid = p.s.groups * p.s.heads * (p.s.tl + (p.s.n_win - 1) * p.s.tf);
+  if constexpr (sizeof(T) == 4) {
+    if (causal)
+      hipLaunchKernelGGL(attn_fwd_k32<true>, dim3(grid), dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL(attn_fwd_k32<false>, dim3(grid), dim3(NTHREADS), 0, stream, p);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_k16<T, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_k16<T, false>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
+                                int S_kv, int D_h, int causal, float scale, int dtype, void* stream,
+                                int chunk, int kv_len) {
+  const int st = validate(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, chunk, kv_len);
+  if (st != ATTN_OK) return st;
+  const int dv = check_device();
+  if (dv != ATTN_OK) return dv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case ATTN_F32:
+      return launch_typed<float>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len);
+    case ATTN_F16:
+      return launch_typed<_Float16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len);
+    default:
+      return launch_typed<__bf16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len);
+  }
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
+                        int D_h, int causal, float scale, int dtype, void* stream) {
+  return attn_fwd_chunked(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, stream, S_q, S_kv);
+}
+
+extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int* grid) {
+  if (B < 1 || H < 1 || S_q < 1 || chunk < 1 || !grid) return ATTN_E_SHAPE;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t n_win = ((int64_t)S_q + chunk - 1) / chunk;
+  const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + BM - 1) / BM);
+  if (bh > (int64_t)INT32_MAX || tiles * bh > (int64_t)INT32_MAX) return ATTN_E_SHAPE;
+  const Sched s = make_sched(B, H, S_q, chunk);
+  *grid = s.groups * s.heads * (s.tl + (s.n_win - 1) * s.tf);
+  return ATTN_OK;
+}
+
+extern "C" int attn_sched_tile(int B, int H, int S_q, int chunk, int block, int* head, int* row0, int* row1) {
+  int grid = 0;
+  const int st = attn_sched_grid(B, H, S_q, chunk, &grid);
+  if (st != ATTN_OK) return st;
+  if (block < 0 || block >= grid || !head || !row0 || !row1) return ATTN_E_SHAPE;
+  decode_tile(make_sched(B, H, S_q, chunk), block, *head, *row0, *row1);
+  return ATTN_OK;
+}
+
+extern "C" const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_E_NULL: return "null tensor pointer";
+    case ATTN_E_SHAPE: return "invalid shape (B, H, S_q, S_kv must be >= 1, D_h must be 64, sizes must fit)";
+    case ATTN_E_DTYPE: return "unknown dtype (expected ATTN_F32, ATTN_F16 or ATTN_BF16)";
+    case ATTN_E_SCALE: return "scale is not finite";
+    case ATTN_E_CAUSAL: return "causal attention needs S_q <= kv_len";
+    case ATTN_E_CHUNK: return "chunk must be >= 1 and kv_len in [1, S_kv]";
+    case ATTN_E_ALIGN: return "tensor base pointer not 16-byte aligned";
+    case ATTN_E_OVERLAP: return "output overlaps an input";
+    case ATTN_E_DEVICE: return "current HIP device missing or not gfx950";
+    case ATTN_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown attn status";
+  }
+}
