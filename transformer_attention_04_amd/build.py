@@ -13,6 +13,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    # device code only: NaN-free arithmetic lets v_max skip canonicalisation
+    "-Xarch_device", "-fno-honor-nans",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

@@ -137,6 +137,76 @@ __device__ __forceinline__ float max_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds_base + 16*l; lds_base must be wave-uniform (it
+// goes to M0).  Issued as inline assembly so the compiler does not add its own
+// conservative waits for it before unrelated LDS reads; completion is tracked
+// explicitly with wait_vmem (vmcnt counts these copies, in issue order).
+__device__ __forceinline__ void dma16(const void* gsrc, const char* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (the direct-to-LDS copies of later tiles may stay in flight).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));  // vmcnt=N, expcnt/lgkmcnt: no wait
+}
+
+// Workgroup barrier that does not drain in-flight direct-to-LDS copies (the
+// fence in __syncthreads would wait for all of them).  LDS reads of this wave
+// are complete before it arrives; the clobbers stop the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void barrier_keep_dma() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14) | (0x0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Online-softmax bookkeeping for one tile, shared by every element type.
+// s holds the raw scores of NB 32-key blocks (16 per lane per block, -inf where
+// masked).  Takes the row maximum (in-lane, then across the two half-waves),
+// raises the exponent offset m only when the tile exceeds it by more than 2^8
+// (then rescales acc and l by exp2(m_old - m_new) for the whole wave), and
+// returns the offset to subtract: 0 while the row has seen no visible key.
+template <int NB>
+__device__ __forceinline__ float online_offset(const f32x16 (&s)[NB], f32x16 (&acc)[2], float& m, float& l,
+                                               const float cc) {
+  float mx[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {  // one chain per block, in two halves
+    float a = fmaxf(s[kb][0], s[kb][1]), b = fmaxf(s[kb][8], s[kb][9]);
+#pragma unroll
+    for (int r = 2; r < 8; ++r) {
+      a = fmaxf(a, s[kb][r]);
+      b = fmaxf(b, s[kb][r + 8]);
+    }
+    mx[kb] = fmaxf(a, b);
+  }
+  float x = mx[0];
+#pragma unroll
+  for (int kb = 1; kb < NB; ++kb) x = fmaxf(x, mx[kb]);
+  x = max_halves(x);
+  const float xc = (x == -INFINITY) ? -INFINITY : x * cc;
+  const bool raise = xc > m + LAZY_TH;
+  if (__any(raise)) {
+    const float m_new = raise ? xc : m;
+    const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf, 1 when unchanged
+    l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[0][r] *= alpha;
+      acc[1][r] *= alpha;
+    }
+    m = m_new;
+  }
+  return (m == -INFINITY) ? 0.f : m;
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit element types
 // ---------------------------------------------------------------------------
@@ -178,11 +248,104 @@ __device__ __forceinline__ int v16_off(int row, int c16) {
   return row * 128 + ((c16 ^ ((row & 3) << 1)) << 4);
 }
 
+// One wave's work on one 64-key tile: S^T = K Q^T on MFMA, online-softmax
+// update, O^T += V^T P^T on MFMA.  TWO: the tile's second 32-key block is
+// visible to some row of this wave (false only on causal diagonal tiles and
+// at the cache end).  MASK: some key of the tile is invisible to some row.
+template <typename T, bool TWO, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void tile16(const char* ks, const char* vs, const typename Half16<T>::vec8 (&qop)[4],
+                                       f32x16 (&acc)[2], float& m, float& l, const float cc,
+                                       const int kv0, const int kv_len, const int pos, const int lane) {
+  typedef Half16<T> H;
+  typedef typename H::vec8 vec8;
+  constexpr int NB = TWO ? 2 : 1;
+  const int c = lane & 31, hf = lane >> 5;
+
+  // S^T = K Q^T; k-step t: lane holds K[32kb + c][32hf + 8t .. +7].
+  f32x16 s[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      const vec8 a = *reinterpret_cast<const vec8*>(ks + k16_off(32 * kb + c, 4 * hf + t));
+      s[kb] = H::mfma(a, qop[t], s[kb]);
+    }
+
+  // V^T operands, read transposed from the [key][d] tile before the softmax
+  // so their latency overlaps it.  Operand (kb, u, dt), k-slot 8hf + e, holds
+  // V[32kb + 16u + 8(e/4) + 4hf + e%4][32dt + c]: source lane s of each
+  // 16-lane group reads row kbase + s/4, columns d0 + 4(s%4) .. +3.
+  vec8 va[NB][2][2];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+          const int c16 = d0 >> 3, half = (d0 >> 2) & 1;
+          const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row + 8, c16) + 8 * half));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          va[kb][u][dt] = __builtin_bit_cast(vec8, aw);
+        }
+  }
+
+  // Mask only diagonal / cache-end tiles: -inf scores give exp2(-inf) = 0.
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const bool vis = key < kv_len && (!CAUSAL || key <= pos);
+        s[kb][r] = vis ? s[kb][r] : -INFINITY;
+      }
+  }
+
+  const float moff = online_offset<NB>(s, acc, m, l, cc);
+
+  // P = exp2(s*c - m) in fp32 (row sum from the fp32 values), RNE-packed to
+  // 16 bits straight into the B operand of step (kb, u): k-slot 8hf + e holds
+  // P[kb][8u + e].  O^T += V^T P^T.
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4 bw;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 8 * u + 2 * q;
+        const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
+        const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
+        ls[q] += e0 + e1;
+        bw[q] = H::pack2(e0, e1);
+      }
+      const vec8 b = __builtin_bit_cast(vec8, bw);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) acc[dt] = H::mfma(va[kb][u][dt], b, acc[dt]);
+    }
+  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
 template <typename T, bool CAUSAL>
 __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
   typedef Half16<T> H;
   typedef typename H::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 128];  // [stage][K,V]
+  // Three LDS stages of one 64-key tile each: K [64][128 B] then V [64][128 B].
+  // Distinct arrays, so reading one stage never waits for copies into another.
+  __shared__ __attribute__((aligned(16))) char st0[2 * 64 * 128];
+  __shared__ __attribute__((aligned(16))) char st1[2 * 64 * 128];
+  __shared__ __attribute__((aligned(16))) char st2[2 * 64 * 128];
 
   int head, row0, row1;
   decode_tile(p.s, blockIdx.x, head, row0, row1);
@@ -190,7 +353,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int c = lane & 31;  // query column of the S^T / O^T tiles
+  const int c = lane & 31;   // query column of the S^T / O^T tiles
   const int hf = lane >> 5;  // half-wave
 
   const T* qh = p.q + (int64_t)head * p.q_head_stride;
@@ -225,32 +388,23 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
     }
   }
 
-  // Global -> register prefetch of one K/V tile: thread owns chunks tid and
-  // tid + 256 of the 512 16-byte chunks of each 8 KB tile.
-  const int ld_row = tid >> 3;  // 0..31 (+32 for the second chunk)
-  const int ld_c16 = tid & 7;
-  u32x4 pk[2], pv[2];
-  auto load_tile = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = kv0 + ld_row + 32 * i;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (row < kv_len) {
-        pk[i] = *reinterpret_cast<const u32x4*>(kh + (int64_t)row * HEAD_DIM + ld_c16 * 8);
-        pv[i] = *reinterpret_cast<const u32x4*>(vh + (int64_t)row * HEAD_DIM + ld_c16 * 8);
-      } else {
-        pk[i] = z;
-        pv[i] = z;
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = ld_row + 32 * i;
-      *reinterpret_cast<u32x4*>(&smem[stage][0][k16_off(row, ld_c16)]) = pk[i];
-      *reinterpret_cast<u32x4*>(&smem[stage][1][v16_off(row, ld_c16)]) = pv[i];
-    }
+  // Tile copies: wave w copies tile rows 8w .. 8w+7 and 32+8w .. 32+8w+7 of K
+  // and of V with one 16-byte direct-to-LDS load per lane each; lane l lands
+  // in row (l / 8), physical chunk (l % 8), so it fetches the logical chunk
+  // that the row's swizzle maps there.  Rows past the cache end re-read row
+  // kv_len - 1 (finite data; those keys are masked).
+  const int drow0 = 8 * wave + (lane >> 3), drow1 = drow0 + 32;
+  const int kch0 = (lane & 7) ^ ((drow0 & 7) ^ ((drow0 >> 3) & 1));
+  const int kch1 = (lane & 7) ^ ((drow1 & 7) ^ ((drow1 >> 3) & 1));
+  const int vch0 = (lane & 7) ^ ((drow0 & 3) << 1);
+  const int vch1 = (lane & 7) ^ ((drow1 & 3) << 1);
+  const int dst0 = 8 * wave * 128, dst1 = (32 + 8 * wave) * 128;
+  auto issue = [&](char* st, int kv0) {
+    const int64_t r0 = min(kv0 + drow0, kv_len - 1), r1 = min(kv0 + drow1, kv_len - 1);
+    dma16(kh + r0 * HEAD_DIM + kch0 * 8, st + dst0);
+    dma16(kh + r1 * HEAD_DIM + kch1 * 8, st + dst1);
+    dma16(vh + r0 * HEAD_DIM + vch0 * 8, st + 64 * 128 + dst0);
+    dma16(vh + r1 * HEAD_DIM + vch1 * 8, st + 64 * 128 + dst1);
   };
 
   f32x16 acc[2];
@@ -261,140 +415,51 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
   }
   float m = -INFINITY;  // exponent offset (log2 units), per row
   float l = 0.f;        // this lane's share of the row sum
-
   const float cc = p.c;
 
-  if (n_tiles > 0) load_tile(0);
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int stage = it & 1;
-    const int kv0 = it * BN;
-    store_tile(stage);
-    if (it + 1 < n_tiles) load_tile(kv0 + BN);
-    __syncthreads();
-
-    // Which 32-key blocks of this tile can any row of this wave see?
-    bool blk[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int first_key = kv0 + 32 * kb;
-      blk[kb] = wave_live && first_key < kv_len && (!CAUSAL || first_key <= pos_last);
+  auto compute = [&](const char* st, int j) {
+    const int kv0 = j * BN;
+    // Which 32-key blocks can some row of this wave see, and does any key of
+    // the tile need masking (cache end, or past the first row's position)?
+    const bool blk0 = wave_live && (!CAUSAL || kv0 <= pos_last);
+    if (!blk0) return;
+    const bool blk1 = kv0 + 32 < kv_len && (!CAUSAL || kv0 + 32 <= pos_last);
+    const int last_key = kv0 + (blk1 ? 63 : 31);
+    const bool need_mask = last_key >= kv_len || (CAUSAL && last_key > pos_first);
+    const char* ks = st;
+    const char* vs = st + 64 * 128;
+    if (blk1) {
+      if (need_mask)
+        tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      else
+        tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+    } else {
+      if (need_mask)
+        tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      else
+        tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
     }
-    if (!blk[0]) continue;  // blk[1] implies blk[0]
-
-    const char* ks = smem[stage][0];
-    const char* vs = smem[stage][1];
-
-    // S^T = K Q^T for the two 32-key blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && !blk[1]) continue;
-        const vec8 a = *reinterpret_cast<const vec8*>(ks + k16_off(32 * kb + c, 4 * hf + t));
-        s[kb] = H::mfma(a, qop[t], s[kb]);
-      }
-    }
-
-    // Masking: only blocks that cross the diagonal or the end of the cache.
-    bool masked = false;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int first_key = kv0 + 32 * kb;
-      const bool need = !blk[kb] || first_key + 31 >= kv_len || (CAUSAL && first_key + 31 > pos_first);
-      if (need) {
-        masked = true;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = first_key + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = blk[kb] && key < kv_len && (!CAUSAL || key <= pos);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
-        }
-      }
-    }
-
-    // Row maximum of the raw scores over the 64 keys.
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_halves(mx);
-    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * cc;
-
-    // Lazy offset update: raise m only when the block exceeds it by > 2^8.
-    const bool raise = mxc > m + LAZY_TH;
-    if (__any(raise)) {
-      const float m_new = raise ? mxc : m;
-      const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf, 1 if unchanged
-      l *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[0][r] *= alpha;
-        acc[1][r] *= alpha;
-      }
-      m = m_new;
-    }
-    const float moff = (m == -INFINITY) ? 0.f : m;
-
-    // P = exp2(s * c - m), row sum, bf16/fp16 pack for the P V operand.
-    unsigned pp[2][8];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
-        float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
-        if (masked) {
-          e0 = (s[kb][r] == -INFINITY) ? 0.f : e0;
-          e1 = (s[kb][r + 1] == -INFINITY) ? 0.f : e1;
-        }
-        lsum += e0 + e1;
-        pp[kb][r >> 1] = H::pack2(e0, e1);
-      }
-    }
-    l += lsum;
-
-    // O^T += V^T P^T.  B operand (k-slot 8*hf + e) is P[kb][8u + e]; the A
-    // operand lane (d, hf) needs V[32kb + 16u + 8(e/4) + 4hf + e%4][d], read
-    // transposed from the [key][d] tile: source lane s of each 16-lane group
-    // reads row kbase + s/4, columns d0 + 4(s%4) .. +3.
-    const int g = lane >> 4;  // 16-lane group
-    const int sl = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb == 1 && !blk[1]) continue;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 bw = {pp[kb][4 * u], pp[kb][4 * u + 1], pp[kb][4 * u + 2], pp[kb][4 * u + 3]};
-        const vec8 b = __builtin_bit_cast(vec8, bw);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
-          const int c16 = d0 >> 3;
-          const int half = (d0 >> 2) & 1;
-          i16x4 lo, hi;
-          {
-            const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
-          }
-          {
-            const int row = 32 * kb + 16 * u + 8 + 4 * (g >> 1) + (sl >> 2);
-            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
-          }
-          u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          acc[dt] = H::mfma(__builtin_bit_cast(vec8, aw), b, acc[dt]);
-        }
-      }
-    }
+  };
+  // Stage j % 3 holds tile j.  At step j: tiles j and j+1 may be in flight;
+  // wait for tile j, barrier (everyone is done with tile j-1), start tile j+2
+  // into tile j-1's stage, compute tile j.
+  auto step = [&](const char* cur, char* nxt, int j) {
+    if (j + 1 < n_tiles)
+      wait_vmem<4>();
+    else
+      wait_vmem<0>();
+    barrier_keep_dma();
+    if (j + 2 < n_tiles) issue(nxt, (j + 2) * BN);
+    compute(cur, j);
+  };
+  if (n_tiles > 0) issue(st0, 0);
+  if (n_tiles > 1) issue(st1, BN);
+  for (int j = 0; j < n_tiles; j += 3) {
+    step(st0, st2, j);
+    if (j + 1 >= n_tiles) break;
+    step(st1, st0, j + 1);
+    if (j + 2 >= n_tiles) break;
+    step(st2, st1, j + 2);
   }
 
   // Epilogue: O = acc / l, RNE to T, rows of this wave that exist.
@@ -420,20 +485,99 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
 // fp32
 // ---------------------------------------------------------------------------
 // LDS tile of 64 rows x 256 bytes (64 floats) = 16 KB, 16 chunks per row.
+// K is XOR-swizzled by row: the S^T operand reads take 16 consecutive rows at
+// one chunk position per access.
 __device__ __forceinline__ int k32_off(int row, int c16) {
   return row * 256 + ((c16 ^ (row & 15)) << 4);
 }
-// V^T reads take one float per lane: 32 consecutive columns from row R (lanes
-// 0-31) and row R+4 (lanes 32-63); the extra bit keeps the two rows' chunks in
-// different halves of the row.
-__device__ __forceinline__ int v32_off(int row, int col) {
-  const int x = (row & 15) ^ (((row >> 2) & 1) << 3);
-  return row * 256 + (((col >> 2) ^ x) << 4) + ((col & 3) << 2);
+// V is stored unswizzled: the P V operand reads take one 256-byte row per
+// 32 lanes (lanes 0-31 row R, lanes 32-63 row R + 4), which is conflict-free
+// as is, and fixed row offsets become immediate address offsets.
+
+// One wave's work on one 64-key fp32 tile (see tile16 for TWO and MASK).
+// The two O^T accumulators hold interleaved columns: acc[dt] row i is
+// d = 2i + dt, so one 8-byte read V[key][2c .. 2c+1] feeds both P V MFMAs.
+template <bool TWO, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void tile32(const char* ks, const char* vs, const float (&qv)[32], f32x16 (&acc)[2],
+                                       float& m, float& l, const float cc, const int kv0, const int kv_len,
+                                       const int pos, const int lane) {
+  constexpr int NB = TWO ? 2 : 1;
+  const int c = lane & 31, hf = lane >> 5;
+
+  // S^T = K Q^T: k-step t contracts d = 32hf + t; lane reads K[32kb + c][32hf .. +31]
+  // as eight 16-byte chunks, each feeding four MFMAs.
+  f32x16 s[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 ka[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(ks + k32_off(32 * kb + c, 8 * hf + j));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ka[kb][e]), qv[4 * j + e], s[kb], 0, 0, 0);
+  }
+
+  // V operands of block 0, read ahead of the softmax: step r of block kb
+  // contracts keys 32kb + 8(r/4) + 4hf + r%4 (k-slot hf), lane (c, hf) needs
+  // V[that key][2c], V[that key][2c + 1].
+  const char* vlane = vs + (4 * hf) * 256 + 8 * c;
+  f32x2 va[NB][16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    va[0][r] = *reinterpret_cast<const f32x2*>(vlane + (8 * (r >> 2) + (r & 3)) * 256);
+
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const bool vis = key < kv_len && (!CAUSAL || key <= pos);
+        s[kb][r] = vis ? s[kb][r] : -INFINITY;
+      }
+  }
+
+  const float moff = online_offset<NB>(s, acc, m, l, cc);
+
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
+      ls[r & 3] += e;
+      s[kb][r] = e;
+    }
+  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+  // O^T += V^T P^T, one key pair per MFMA: k-slot hf of step r is this lane's
+  // probability s[kb][r].  Block 1's operands are read during block 0's MFMAs.
+  if constexpr (TWO) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      va[1][r] = *reinterpret_cast<const f32x2*>(vlane + (32 + 8 * (r >> 2) + (r & 3)) * 256);
+  }
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[kb][r][0], s[kb][r], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[kb][r][1], s[kb][r], acc[1], 0, 0, 0);
+    }
 }
 
 template <bool CAUSAL>
-__global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k32(Params<float> p) {
-  __shared__ __attribute__((aligned(16))) char smem[2][2][64 * 256];  // [stage][K,V]
+__global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_k32(Params<float> p) {
+  // Three LDS stages of one 64-key tile each: K [64][256 B] then V [64][256 B].
+  __shared__ __attribute__((aligned(16))) char st0[2 * 64 * 256];
+  __shared__ __attribute__((aligned(16))) char st1[2 * 64 * 256];
+  __shared__ __attribute__((aligned(16))) char st2[2 * 64 * 256];
 
   int head, row0, row1;
   decode_tile(p.s, blockIdx.x, head, row0, row1);
@@ -478,30 +622,24 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k32(Params<float> p) {
     }
   }
 
-  // thread owns chunks tid + 256 i (i < 4) of the 1024 16-byte chunks of a tile
-  const int ld_row = tid >> 4;  // 0..15 (+16 i)
-  const int ld_c16 = tid & 15;
-  u32x4 pk[4], pv[4];
-  auto load_tile = [&](int kv0) {
+  // Tile copies: wave w, copy i < 4 fills tile rows 4(4i + w) .. +3 (one
+  // 256-byte row per 16 lanes); lane l lands in row + l/16, physical chunk
+  // l % 16 and fetches the logical chunk the row's swizzle maps there.
+  int krow[4], kch[4], vch[4], dst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (4 * i + wave) + (lane >> 4);
+    krow[i] = row;
+    kch[i] = (lane & 15) ^ (row & 15);
+    vch[i] = lane & 15;
+    dst[i] = 4 * (4 * i + wave) * 256;
+  }
+  auto issue = [&](char* st, int kv0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = kv0 + ld_row + 16 * i;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (row < kv_len) {
-        pk[i] = *reinterpret_cast<const u32x4*>(kh + (int64_t)row * HEAD_DIM + ld_c16 * 4);
-        pv[i] = *reinterpret_cast<const u32x4*>(vh + (int64_t)row * HEAD_DIM + ld_c16 * 4);
-      } else {
-        pk[i] = z;
-        pv[i] = z;
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = ld_row + 16 * i;
-      *reinterpret_cast<u32x4*>(&smem[stage][0][k32_off(row, ld_c16)]) = pk[i];
-      *reinterpret_cast<u32x4*>(&smem[stage][1][v32_off(row, 4 * ld_c16)]) = pv[i];
+      const int64_t r = min(kv0 + krow[i], kv_len - 1);
+      dma16(kh + r * HEAD_DIM + kch[i] * 4, st + dst[i]);
+      dma16(vh + r * HEAD_DIM + vch[i] * 4, st + 64 * 256 + dst[i]);
     }
   };
 
@@ -515,128 +653,67 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k32(Params<float> p) {
   float l = 0.f;
   const float cc = p.c;
 
-  if (n_tiles > 0) load_tile(0);
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int stage = it & 1;
-    const int kv0 = it * BN;
-    store_tile(stage);
-    if (it + 1 < n_tiles) load_tile(kv0 + BN);
-    __syncthreads();
-
-    bool blk[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int first_key = kv0 + 32 * kb;
-      blk[kb] = wave_live && first_key < kv_len && (!CAUSAL || first_key <= pos_last);
+  auto compute = [&](const char* st, int j) {
+    const int kv0 = j * BN;
+    const bool blk0 = wave_live && (!CAUSAL || kv0 <= pos_last);
+    if (!blk0) return;
+    const bool blk1 = kv0 + 32 < kv_len && (!CAUSAL || kv0 + 32 <= pos_last);
+    const int last_key = kv0 + (blk1 ? 63 : 31);
+    const bool need_mask = last_key >= kv_len || (CAUSAL && last_key > pos_first);
+    const char* ks = st;
+    const char* vs = st + 64 * 256;
+    if (blk1) {
+      if (need_mask)
+        tile32<true, true, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
+      else
+        tile32<true, false, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
+    } else {
+      if (need_mask)
+        tile32<false, true, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
+      else
+        tile32<false, false, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
     }
-    if (!blk[0]) continue;
-
-    const char* ks = smem[stage][0];
-    const char* vs = smem[stage][1];
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && !blk[1]) continue;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + k32_off(32 * kb + c, 8 * hf + j));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), qv[4 * j + e], s[kb], 0, 0, 0);
-      }
-    }
-
-    bool masked = false;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int first_key = kv0 + 32 * kb;
-      const bool need = !blk[kb] || first_key + 31 >= kv_len || (CAUSAL && first_key + 31 > pos_first);
-      if (need) {
-        masked = true;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = first_key + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = blk[kb] && key < kv_len && (!CAUSAL || key <= pos);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
-        }
-      }
-    }
-
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_halves(mx);
-    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * cc;
-
-    const bool raise = mxc > m + LAZY_TH;
-    if (__any(raise)) {
-      const float m_new = raise ? mxc : m;
-      const float alpha = fast_exp2(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[0][r] *= alpha;
-        acc[1][r] *= alpha;
-      }
-      m = m_new;
-    }
-    const float moff = (m == -INFINITY) ? 0.f : m;
-
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
-        if (masked) e = (s[kb][r] == -INFINITY) ? 0.f : e;
-        lsum += e;
-        s[kb][r] = e;
-      }
-    }
-    l += lsum;
-
-    // O^T += V^T P^T, one key pair per MFMA: k-slot hf of step r is key
-    // 32kb + 8(r/4) + 4hf + r%4, whose probability is this lane's s[kb][r].
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb == 1 && !blk[1]) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const float a = *reinterpret_cast<const float*>(vs + v32_off(key, 32 * dt + c));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][r], acc[dt], 0, 0, 0);
-        }
-      }
-    }
+  };
+  // Same three-stage schedule as the 16-bit kernel; 8 copies per tile per wave.
+  auto step = [&](const char* cur, char* nxt, int j) {
+    if (j + 1 < n_tiles)
+      wait_vmem<8>();
+    else
+      wait_vmem<0>();
+    barrier_keep_dma();
+    if (j + 2 < n_tiles) issue(nxt, (j + 2) * BN);
+    compute(cur, j);
+  };
+  if (n_tiles > 0) issue(st0, 0);
+  if (n_tiles > 1) issue(st1, BN);
+  for (int j = 0; j < n_tiles; j += 3) {
+    step(st0, st2, j);
+    if (j + 1 >= n_tiles) break;
+    step(st1, st0, j + 1);
+    if (j + 2 >= n_tiles) break;
+    step(st2, st1, j + 2);
   }
 
   const float lt = l + other_half(l);
   const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
   if (qrow < row1) {
+    // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
+    // 4g .. 4g+3 of both accumulators cover columns 16g + 8hf .. +7.
     float* orow = oh + (int64_t)qrow * HEAD_DIM;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * dt + 8 * gq + 4 * hf;
-        u32x4 w;
-        w[0] = __float_as_uint(acc[dt][4 * gq] * inv);
-        w[1] = __float_as_uint(acc[dt][4 * gq + 1] * inv);
-        w[2] = __float_as_uint(acc[dt][4 * gq + 2] * inv);
-        w[3] = __float_as_uint(acc[dt][4 * gq + 3] * inv);
-        *reinterpret_cast<u32x4*>(orow + d) = w;
-      }
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 16 * gq + 8 * hf;
+      u32x4 w0, w1;
+      w0[0] = __float_as_uint(acc[0][4 * gq] * inv);
+      w0[1] = __float_as_uint(acc[1][4 * gq] * inv);
+      w0[2] = __float_as_uint(acc[0][4 * gq + 1] * inv);
+      w0[3] = __float_as_uint(acc[1][4 * gq + 1] * inv);
+      w1[0] = __float_as_uint(acc[0][4 * gq + 2] * inv);
+      w1[1] = __float_as_uint(acc[1][4 * gq + 2] * inv);
+      w1[2] = __float_as_uint(acc[0][4 * gq + 3] * inv);
+      w1[3] = __float_as_uint(acc[1][4 * gq + 3] * inv);
+      *reinterpret_cast<u32x4*>(orow + d) = w0;
+      *reinterpret_cast<u32x4*>(orow + d + 4) = w1;
     }
   }
 }
@@ -718,7 +795,10 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   p.kv_head_stride = (int64_t)S_kv * HEAD_DIM;
   p.S_q = S_q;
   p.kv_len = kv_len;
-  p.c = (float)(std::fabs((double)scale) * 1.4426950408889634);
+  // |scale| * log2(e), at least 1e-30 so that a masked score (-inf) always
+  // exponentiates to 0; for scale = 0 every visible probability is still
+  // exp2(~1e-27) = 1 exactly in fp32.
+  p.c = (float)std::max(std::fabs((double)scale) * 1.4426950408889634, 1e-30);
   p.q_flip = (scale < 0.f) ? (sizeof(T) == 4 ? 0x80000000u : 0x80008000u) : 0u;
   p.s = make_sched(B, H, S_q, chunk);
   const int grid = p.s.groups * p.s.heads * (p.s.tl + (p.s.n_win - 1) * p.s.tf);
