@@ -49,7 +49,34 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--copy-mb", type=float, default=None,
+                    help="instead of attention, time a plain device copy of this many MB per step "
+                         "(reference kernel of known traffic for scaling HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration(args):
+    """A plain copy kernel of known size: each step reads and writes copy_mb MB."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = int(args.copy_mb * 1e6) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    line = {"metric": "device copy GB/s (read + write)", "value": round(2 * n * 4 / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "bytes_read_per_step": n * 4, "bytes_written_per_step": n * 4,
+            "ms_per_step": round(ms, 6), "steps": args.steps}
+    print(json.dumps(line), flush=True)
 
 
 def roofline_for(w, dtype, sec_per_call):
@@ -67,6 +94,23 @@ def roofline_for(w, dtype, sec_per_call):
             "frac": round(ach / pk, 4), "traffic": None}
 
 
+def measured_traffic(workload, dtype):
+    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
+    or None when there is no entry or the kernel source changed since."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            t = json.load(f)
+        with open(os.path.join(ROOT, t["kernel_source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, KeyError, ValueError):
+        return None
+    e = t.get("entries", {}).get(f"{workload}/{dtype}")
+    if e is None or sha != t.get("source_sha256_16"):
+        return None
+    return e["traffic_bytes"]
+
+
 def cpu_baseline(w, dtype, budget_s):
     """Time the fp64 oracle on a bounded sample of the workload's query rows."""
     import numpy as np
@@ -81,31 +125,30 @@ def cpu_baseline(w, dtype, budget_s):
                          w.outlier_frac, w.outlier_mult)
         q, k, v = W.make_inputs(one, dtype)
     heads = q.shape[0] * q.shape[1]
-    # calibrate on a few rows, then size the sample to the time budget
-    rows_all = np.arange(w.S_q)
+    # Time batches of randomly drawn query rows (all heads of the sample) until
+    # the budget is used; a sample that covers every row repeats whole runs.
     rng = np.random.default_rng(0)
+    order = rng.permutation(w.S_q)
+    batch = max(1, min(w.S_q, (1 << 26) // (w.S_kv * heads)))  # ~2^26 (row, key) pairs per batch
+    done, reps, pos = [], 0, 0
     t0 = time.perf_counter()
-    probe = np.sort(rng.choice(rows_all, size=min(w.S_q, 8), replace=False))
-    oracle.attention(q, k, v, causal=w.causal, scale=w.scale, rows=probe, threads=threads)
-    dt = max(time.perf_counter() - t0, 1e-4)
-    per_row_head = dt / (len(probe) * heads)
-    n_rows = int(min(w.S_q, max(1, budget_s / (per_row_head * heads))))
-    rows = np.sort(rng.choice(rows_all, size=n_rows, replace=False)) if n_rows < w.S_q else None
-    reps = 0
-    t0 = time.perf_counter()
-    while True:  # a sample that covers the whole workload repeats until the budget is used
+    while True:
+        rows = np.sort(order[pos:pos + batch])
         oracle.attention(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
-        reps += 1
+        done.append(rows)
+        pos += batch
+        if pos >= w.S_q:
+            pos, reps = 0, reps + 1
         el = time.perf_counter() - t0
-        if rows is not None or el >= budget_s:
+        if el >= budget_s:
             break
+    r = np.concatenate(done)
     # counted FLOPs of the sampled rows: 4*D per visible (row, key) pair
     shift = w.S_kv - w.S_q
-    r = rows_all if rows is None else rows
     vis = (np.minimum(r + shift + 1, w.S_kv) if w.causal else np.full(len(r), w.S_kv)).sum()
-    flops = 4.0 * w.D * float(vis) * heads * reps
+    flops = 4.0 * w.D * float(vis) * heads
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} head(s) x {len(r)} of {w.S_q} query rows x {reps} run(s) "
+            "sample": f"{heads} head(s) x {len(r)} query-row evaluations (rows of {w.S_q}, in random order) "
                       f"({flops / 1e9:.2f} GFLOP counted, {el:.1f} s, fp64)",
             "seconds": round(el, 3)}
 
@@ -116,6 +159,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(no multi-GPU path exists in this library)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mb:
+        copy_calibration(args)
+        return
     import torch
     import workloads as W
     import transformer_attention_04_amd as A
@@ -175,6 +221,7 @@ def main():
                    "causal": w.causal, "chunk": w.chunk, "rotating_sets": len(sets)},
         "roofline": roofline_for(w, dtype, sec),
     }
+    line["roofline"]["traffic"] = measured_traffic(w.name, dtype)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)
