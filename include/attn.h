@@ -91,7 +91,10 @@ enum attn_status {
  *   dtype      : enum attn_dtype of all four tensors.
  *   stream     : hipStream_t to enqueue on (NULL = null stream).
  * Identical, bit for bit, to attn_fwd_chunked(..., chunk = S_q,
- * kv_len = S_kv).
+ * kv_len = S_kv).  When B*H*ceil(S_q/128) is at most twice the number of
+ * compute units, each 128-row query tile's keys are split between two wave
+ * groups and merged at the end (more parallelism for small grids); the split
+ * depends on B, H and S_q only.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o,
              int B, int H, int S_q, int S_kv, int D_h,
@@ -111,7 +114,9 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o,
  * kv_len (no workspace).  The window split changes the schedule, not the
  * result: each output row is bit-identical to attn_fwd's on the same data.
  * A streaming caller appends a window's K/V rows to the cache and calls with
- * S_q = that window's rows and the grown kv_len.
+ * S_q = that window's rows and the grown kv_len; its rows equal the single
+ * call's bit for bit when both calls make the same key-split choice (see
+ * attn_fwd), and to rounding otherwise.
  */
 int attn_fwd_chunked(const void *q, const void *k, const void *v, void *o,
                      int B, int H, int S_q, int S_kv, int D_h,
@@ -121,14 +126,17 @@ int attn_fwd_chunked(const void *q, const void *k, const void *v, void *o,
 /*
  * Schedule introspection (host only, no GPU needed).  attn_sched_grid writes the
  * number of workgroups one attn_fwd_chunked call with these sizes launches
- * (attn_fwd: chunk = S_q); attn_sched_tile writes which head (b*H + h) and
- * which query rows [row0, row1) workgroup `block` computes.  Every (head, row)
- * is covered by exactly one workgroup.  Both return ATTN_OK, or ATTN_E_SHAPE
- * for sizes out of range or a NULL output pointer.
+ * (attn_fwd: chunk = S_q, kv_len = S_kv; causal as in the call, 0/1);
+ * attn_sched_tile writes which head
+ * (b*H + h) and which query rows [row0, row1) workgroup `block` computes.
+ * Every (head, row) is covered by exactly one workgroup; windows run heaviest
+ * first.  Both return ATTN_OK, or ATTN_E_SHAPE for sizes out of range or a
+ * NULL output pointer.
  */
-int attn_sched_grid(int B, int H, int S_q, int chunk, int *grid);
-int attn_sched_tile(int B, int H, int S_q, int chunk, int block,
-                    int *head, int *row0, int *row1);
+int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal,
+                    int *grid);
+int attn_sched_tile(int B, int H, int S_q, int chunk, int kv_len, int causal,
+                    int block, int *head, int *row0, int *row1);
 
 /* Static, NUL-terminated description of an attn_status value (never NULL). */
 const char *attn_strerror(int status);

@@ -92,17 +92,22 @@ def test_noncausal_allows_more_queries_than_keys():
     assert call(causal=0, S_q=500, kv_len=7) == 9  # passes validation, stops at the device check
 
 
-@pytest.mark.parametrize("B,H,S_q,chunk", [
-    (1, 1, 1, 1), (1, 1, 128, 128), (1, 1, 129, 129), (2, 3, 300, 64), (2, 4, 300, 100),
-    (1, 8, 1000, 7), (4, 8, 2048, 2048), (8, 8, 512, 512), (3, 5, 777, 256), (2, 8, 5000, 4096),
-    (1, 16, 4096, 1000), (16, 1, 64, 1),
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,H,S_q,chunk,kv_len", [
+    (1, 1, 1, 1, 1), (1, 1, 128, 128, 128), (1, 1, 129, 129, 129), (2, 3, 300, 64, 300), (2, 4, 300, 100, 300),
+    (1, 8, 1000, 7, 1000), (4, 8, 2048, 2048, 2048), (8, 8, 512, 512, 512), (3, 5, 777, 256, 777),
+    (2, 8, 5000, 4096, 20000), (1, 16, 4096, 1000, 4096), (16, 1, 64, 1, 64), (2, 8, 3000, 1000, 9000),
 ])
-def test_schedule_covers_every_row_once(B, H, S_q, chunk):
-    grid = A.sched_grid(B, H, S_q, chunk)
+def test_schedule_covers_every_row_once(B, H, S_q, chunk, kv_len, causal):
+    grid = A.sched_grid(B, H, S_q, chunk, kv_len, causal)
     seen = {}
     n_win = -(-S_q // chunk)
+    tile_major = causal and kv_len <= 8192
+    groups = 8 if (B * H) % 8 == 0 else 1
+    seq = {g: [] for g in range(groups)}
     for blk in range(grid):
-        h, r0, r1 = A.sched_tile(B, H, S_q, chunk, blk)
+        h, r0, r1 = A.sched_tile(B, H, S_q, chunk, blk, kv_len, causal)
+        seq[blk % groups].append((r0 // chunk, r0, h))
         assert 0 <= h < B * H and 0 <= r0 < r1 <= S_q and r1 - r0 <= 128
         assert r0 // chunk == (r1 - 1) // chunk, "tile straddles a window"
         seen.setdefault(h, []).append((r0, r1))
@@ -116,18 +121,30 @@ def test_schedule_covers_every_row_once(B, H, S_q, chunk):
             assert r0 == pos
             pos = r1
         assert pos == S_q
-    # heaviest window first: window index never increases along each XCD's sequence
-    groups = 8 if (B * H) % 8 == 0 else 1
-    for g in range(groups):
-        wins = [A.sched_tile(B, H, S_q, chunk, b)[1] // chunk for b in range(g, grid, groups)]
+    # along each XCD's sequence: heaviest window first; inside a window the
+    # last tile first, either for all heads at once (short caches: tile-major)
+    # or one head at a time (long caches: head-major)
+    for g, items in seq.items():
+        wins = [w for w, _, _ in items]
         assert wins == sorted(wins, reverse=True)
-    assert n_win == len({A.sched_tile(B, H, S_q, chunk, b)[1] // chunk for b in range(grid)})
+        for w in set(wins):
+            inside = [(r0, h) for ww, r0, h in items if ww == w]
+            if tile_major:
+                rows = [r0 for r0, _ in inside]
+                assert rows == sorted(rows, reverse=True)
+            else:
+                heads = [h for _, h in inside]
+                assert heads == sorted(heads), "head-major order broken"
+                for hh in set(heads):
+                    rows = [r0 for r0, h in inside if h == hh]
+                    assert rows == sorted(rows, reverse=True)
+    assert n_win == len({w for items in seq.values() for w, _, _ in items})
 
 
 def test_long_context_grid_size():
     # 98,304 rows in 4,096-row windows, 128-row tiles, 256 heads
-    assert A.sched_grid(16, 16, 98304, 4096) == 24 * 32 * 256
-    assert A.sched_grid(16, 16, 98304, 98304) == 768 * 256
+    assert A.sched_grid(16, 16, 98304, 4096, 98304) == 24 * 32 * 256
+    assert A.sched_grid(16, 16, 98304, 98304, 98304) == 768 * 256
 
 
 def test_binding_refuses_missing_library(tmp_path):

@@ -100,6 +100,31 @@ def test_edge_shapes(dtype):
     say(f"[parity] edge shapes {dtype}: worst err/bound {worst:.3f}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_many_tile_grids(dtype):
+    """Grids with more than two 128-row tiles per CU take the unsplit kernel
+    (every wave walks all keys); small grids split keys between two wave
+    groups.  Cover the unsplit path for every dtype, causal and not, with
+    ragged sizes and a partly filled cache."""
+    w = W.Workload("grid", 16, 16, 300, 333, 64, True, (dtype,), seed=61)
+    q, k, v = W.make_inputs(w, dtype)
+    for causal in (False, True):
+        check(q, k, v, dtype, causal, what=f"16x16 heads causal={causal}")
+    check(q, k, v, dtype, True, chunk=100, kv_len=320, what="16x16 heads chunk 100 kv_len 320")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causal_offsets(dtype):
+    """Bottom-right causal with S_kv - S_q in {1 .. 100}: some query rows see no
+    key of a whole 64-key tile that other rows of their wave do see (a wave
+    whose first tile is such a tile starts with rows that have seen nothing)."""
+    for n, off in enumerate((1, 2, 31, 32, 33, 63, 64, 65, 100)):
+        w = W.Workload("off", 2, 3, 200, 200 + off, 64, True, (dtype,), seed=700 + n)
+        q, k, v = W.make_inputs(w, dtype)
+        check(q, k, v, dtype, True, what=f"causal offset {off}")
+        check(q, k, v, dtype, True, chunk=64, kv_len=200 + off, what=f"causal offset {off} chunk 64")
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 1e-3])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_scales(dtype, scale):

@@ -49,9 +49,9 @@ def _load(path: str = LIB_PATH):
     lib.attn_fwd_chunked.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
-    lib.attn_sched_grid.argtypes = [i, i, i, i, ctypes.POINTER(i)]
+    lib.attn_sched_grid.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i)]
     lib.attn_sched_grid.restype = i
-    lib.attn_sched_tile.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.attn_sched_tile.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.attn_sched_tile.restype = i
     return lib
 
@@ -135,17 +135,19 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     return o
 
 
-def sched_grid(B: int, H: int, S_q: int, chunk: int) -> int:
+def sched_grid(B: int, H: int, S_q: int, chunk: int, kv_len: int | None = None, causal: bool = True) -> int:
     g = ctypes.c_int()
-    st = lib.attn_sched_grid(B, H, S_q, chunk, ctypes.byref(g))
+    st = lib.attn_sched_grid(B, H, S_q, chunk, S_q if kv_len is None else kv_len, int(bool(causal)), ctypes.byref(g))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return g.value
 
 
-def sched_tile(B: int, H: int, S_q: int, chunk: int, block: int):
+def sched_tile(B: int, H: int, S_q: int, chunk: int, block: int, kv_len: int | None = None,
+               causal: bool = True):
     h, r0, r1 = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    st = lib.attn_sched_tile(B, H, S_q, chunk, block, ctypes.byref(h), ctypes.byref(r0), ctypes.byref(r1))
+    st = lib.attn_sched_tile(B, H, S_q, chunk, S_q if kv_len is None else kv_len, int(bool(causal)), block,
+                             ctypes.byref(h), ctypes.byref(r0), ctypes.byref(r1))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return h.value, r0.value, r1.value

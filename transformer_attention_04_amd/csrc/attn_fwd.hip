@@ -39,6 +39,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -65,19 +66,26 @@ constexpr float LAZY_TH = 8.0f;  // log2 headroom before the offset is raised
 // ---------------------------------------------------------------------------
 // Schedule: blockIdx.x -> (head, query rows [row0, row1)).
 // Windows are enqueued heaviest first (the last window sees the longest key
-// prefix when causal); inside a window tiles run from the diagonal end
-// backwards.  When B*H is a multiple of 8, head h only runs on XCD h % 8
-// (workgroups are dealt to the 8 XCDs round-robin by id), so the query tiles
-// of one head share that XCD's L2 for their common K/V prefix.
+// prefix when causal).  Inside a window, causal calls on short caches go
+// tile-major: every head's last (heaviest) 128-row tile, then every head's
+// next one, so the dispatcher approximates longest-job-first.  Otherwise
+// (equal-cost tiles, or long caches) windows go head-major: one head's tiles
+// back to back, last tile first, so the tiles sharing a K/V prefix run
+// together while it is in L2.  When B*H is a multiple of 8, head
+// h only runs on XCD h % 8 (workgroups are dealt to the 8 XCDs round-robin by
+// id), so the query tiles of one head share that XCD's L2.
 // ---------------------------------------------------------------------------
+constexpr int TILE_MAJOR_MAX_KV = 8192;  // cache rows up to which causal windows go tile-major
+
 struct Sched {
   int S_q;
-  int chunk;   // rows per window
-  int n_win;   // windows
-  int tf;      // tiles per full window
-  int tl;      // tiles in the last window
-  int heads;   // heads enumerated per decode group
-  int groups;  // 8 (XCD-grouped) or 1
+  int chunk;       // rows per window
+  int n_win;       // windows
+  int tf;          // tiles per full window
+  int tl;          // tiles in the last window
+  int heads;       // heads enumerated per decode group
+  int groups;      // 8 (XCD-grouped) or 1
+  int tile_major;  // order inside a window
 };
 
 __host__ __device__ inline void decode_tile(const Sched& s, int b, int& head, int& row0, int& row1) {
@@ -88,19 +96,26 @@ __host__ __device__ inline void decode_tile(const Sched& s, int b, int& head, in
   }
   const int last = s.n_win - 1;
   const int n_last = s.heads * s.tl;
-  int w, j, t;
+  int w, rem, tw;  // window, position inside it, tiles per head in it
   if (L < n_last) {
     w = last;
-    j = L / s.tl;
-    t = s.tl - 1 - (L - j * s.tl);
+    rem = L;
+    tw = s.tl;
   } else {
     const int L2 = L - n_last;
     const int per = s.heads * s.tf;
     const int wi = L2 / per;
-    const int rem = L2 - wi * per;
+    rem = L2 - wi * per;
     w = last - 1 - wi;
-    j = rem / s.tf;
-    t = s.tf - 1 - (rem - j * s.tf);
+    tw = s.tf;
+  }
+  int j, t;
+  if (s.tile_major) {
+    t = tw - 1 - rem / s.heads;
+    j = rem - (rem / s.heads) * s.heads;
+  } else {
+    j = rem / tw;
+    t = tw - 1 - (rem - j * tw);
   }
   head = j * s.groups + grp;
   const int wstart = w * s.chunk;
@@ -194,8 +209,11 @@ __device__ __forceinline__ float online_offset(const f32x16 (&s)[NB], f32x16 (&a
   const float xc = (x == -INFINITY) ? -INFINITY : x * cc;
   const bool raise = xc > m + LAZY_TH;
   if (__any(raise)) {
+    // Raising lanes scale by exp2(m - xc) (0 when m was -inf); the others keep
+    // their offset and scale by exactly 1 (m may still be -inf there: rows
+    // that have not seen a visible key yet, so m - m would be NaN).
     const float m_new = raise ? xc : m;
-    const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf, 1 when unchanged
+    const float alpha = raise ? fast_exp2(m - xc) : 1.f;
     l *= alpha;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -337,150 +355,6 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
   l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
-template <typename T, bool CAUSAL>
-__global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_k16(Params<T> p) {
-  typedef Half16<T> H;
-  typedef typename H::vec8 vec8;
-  // Three LDS stages of one 64-key tile each: K [64][128 B] then V [64][128 B].
-  // Distinct arrays, so reading one stage never waits for copies into another.
-  __shared__ __attribute__((aligned(16))) char st0[2 * 64 * 128];
-  __shared__ __attribute__((aligned(16))) char st1[2 * 64 * 128];
-  __shared__ __attribute__((aligned(16))) char st2[2 * 64 * 128];
-
-  int head, row0, row1;
-  decode_tile(p.s, blockIdx.x, head, row0, row1);
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int c = lane & 31;   // query column of the S^T / O^T tiles
-  const int hf = lane >> 5;  // half-wave
-
-  const T* qh = p.q + (int64_t)head * p.q_head_stride;
-  const T* kh = p.k + (int64_t)head * p.kv_head_stride;
-  const T* vh = p.v + (int64_t)head * p.kv_head_stride;
-  T* oh = p.o + (int64_t)head * p.q_head_stride;
-
-  const int kv_len = p.kv_len;
-  const int shift = kv_len - p.S_q;  // absolute position of query row r is r + shift
-  const int kv_end = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
-  const int n_tiles = (kv_end + BN - 1) / BN;
-
-  // This wave's query rows and their positions.
-  const int wrow0 = row0 + wave * 32;
-  const int qrow = wrow0 + c;
-  const bool wave_live = wrow0 < row1;
-  const int wlast = min(wrow0 + 31, row1 - 1);  // last valid row of the wave
-  const int pos = qrow + shift;
-  const int pos_first = wrow0 + shift;
-  const int pos_last = wlast + shift;
-
-  // Q^T operand: lane holds Q[qrow][32*hf + 8*t .. +7] for k-step t.
-  vec8 qop[4];
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * HEAD_DIM + 32 * hf);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < row1) x = src[t];
-      x ^= p.q_flip;
-      qop[t] = __builtin_bit_cast(vec8, x);
-    }
-  }
-
-  // Tile copies: wave w copies tile rows 8w .. 8w+7 and 32+8w .. 32+8w+7 of K
-  // and of V with one 16-byte direct-to-LDS load per lane each; lane l lands
-  // in row (l / 8), physical chunk (l % 8), so it fetches the logical chunk
-  // that the row's swizzle maps there.  Rows past the cache end re-read row
-  // kv_len - 1 (finite data; those keys are masked).
-  const int drow0 = 8 * wave + (lane >> 3), drow1 = drow0 + 32;
-  const int kch0 = (lane & 7) ^ ((drow0 & 7) ^ ((drow0 >> 3) & 1));
-  const int kch1 = (lane & 7) ^ ((drow1 & 7) ^ ((drow1 >> 3) & 1));
-  const int vch0 = (lane & 7) ^ ((drow0 & 3) << 1);
-  const int vch1 = (lane & 7) ^ ((drow1 & 3) << 1);
-  const int dst0 = 8 * wave * 128, dst1 = (32 + 8 * wave) * 128;
-  auto issue = [&](char* st, int kv0) {
-    const int64_t r0 = min(kv0 + drow0, kv_len - 1), r1 = min(kv0 + drow1, kv_len - 1);
-    dma16(kh + r0 * HEAD_DIM + kch0 * 8, st + dst0);
-    dma16(kh + r1 * HEAD_DIM + kch1 * 8, st + dst1);
-    dma16(vh + r0 * HEAD_DIM + vch0 * 8, st + 64 * 128 + dst0);
-    dma16(vh + r1 * HEAD_DIM + vch1 * 8, st + 64 * 128 + dst1);
-  };
-
-  f32x16 acc[2];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc[0][r] = 0.f;
-    acc[1][r] = 0.f;
-  }
-  float m = -INFINITY;  // exponent offset (log2 units), per row
-  float l = 0.f;        // this lane's share of the row sum
-  const float cc = p.c;
-
-  auto compute = [&](const char* st, int j) {
-    const int kv0 = j * BN;
-    // Which 32-key blocks can some row of this wave see, and does any key of
-    // the tile need masking (cache end, or past the first row's position)?
-    const bool blk0 = wave_live && (!CAUSAL || kv0 <= pos_last);
-    if (!blk0) return;
-    const bool blk1 = kv0 + 32 < kv_len && (!CAUSAL || kv0 + 32 <= pos_last);
-    const int last_key = kv0 + (blk1 ? 63 : 31);
-    const bool need_mask = last_key >= kv_len || (CAUSAL && last_key > pos_first);
-    const char* ks = st;
-    const char* vs = st + 64 * 128;
-    if (blk1) {
-      if (need_mask)
-        tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
-      else
-        tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
-    } else {
-      if (need_mask)
-        tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
-      else
-        tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
-    }
-  };
-  // Stage j % 3 holds tile j.  At step j: tiles j and j+1 may be in flight;
-  // wait for tile j, barrier (everyone is done with tile j-1), start tile j+2
-  // into tile j-1's stage, compute tile j.
-  auto step = [&](const char* cur, char* nxt, int j) {
-    if (j + 1 < n_tiles)
-      wait_vmem<4>();
-    else
-      wait_vmem<0>();
-    barrier_keep_dma();
-    if (j + 2 < n_tiles) issue(nxt, (j + 2) * BN);
-    compute(cur, j);
-  };
-  if (n_tiles > 0) issue(st0, 0);
-  if (n_tiles > 1) issue(st1, BN);
-  for (int j = 0; j < n_tiles; j += 3) {
-    step(st0, st2, j);
-    if (j + 1 >= n_tiles) break;
-    step(st1, st0, j + 1);
-    if (j + 2 >= n_tiles) break;
-    step(st2, st1, j + 2);
-  }
-
-  // Epilogue: O = acc / l, RNE to T, rows of this wave that exist.
-  const float lt = l + other_half(l);
-  const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
-  if (qrow < row1) {
-    T* orow = oh + (int64_t)qrow * HEAD_DIM;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * dt + 8 * gq + 4 * hf;
-        u32x2 w;
-        w[0] = H::pack2(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv);
-        w[1] = H::pack2(acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // fp32
 // ---------------------------------------------------------------------------
@@ -572,74 +446,112 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
     }
 }
 
-template <bool CAUSAL>
-__global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_k32(Params<float> p) {
-  // Three LDS stages of one 64-key tile each: K [64][256 B] then V [64][256 B].
-  __shared__ __attribute__((aligned(16))) char st0[2 * 64 * 256];
-  __shared__ __attribute__((aligned(16))) char st1[2 * 64 * 256];
-  __shared__ __attribute__((aligned(16))) char st2[2 * 64 * 256];
+// ---------------------------------------------------------------------------
+// The kernel (all element types)
+// ---------------------------------------------------------------------------
+// KS = 1: 4 wavefronts, one per 32 query rows; each wave walks every key tile.
+// KS = 2: 8 wavefronts; waves 4..7 take the same query rows as waves 0..3 but
+// the odd 64-key tiles while waves 0..3 take the even ones, and the two
+// partial (m, l, acc) states are merged through LDS at the end.  This halves
+// the sequential key chain per wave when there are too few workgroups to
+// fill the GPU.
+//
+// Pipeline: a stage holds KS consecutive 64-key tiles of K, then of V.  With
+// three stages two stages are in flight while one is computed; with two, one.
+template <typename T, bool CAUSAL, int KS>
+__global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2 : 1)
+    attn_fwd_kernel(Params<T> p) {
+  constexpr bool F32 = sizeof(T) == 4;
+  constexpr int ROWB = F32 ? 256 : 128;  // bytes per K/V row (64 elements)
+  constexpr int TILE = 64 * ROWB;        // one 64-row tile of K or V
+  constexpr int STAGE = 2 * KS * TILE;   // KS K tiles, then KS V tiles
+  constexpr int NS = KS == 1 ? 3 : 2;    // LDS stages
+  constexpr int LPR = ROWB / 16;         // lanes per row in one 16-byte-per-lane copy
+  constexpr int RPC = 64 / LPR;          // rows per copy instruction
+  constexpr int NCP = ROWB / 64;         // copies per wave per matrix per stage
+  // Distinct arrays: reading one stage never waits for copies into another.
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[NS == 3 ? STAGE : 16];
 
   int head, row0, row1;
   decode_tile(p.s, blockIdx.x, head, row0, row1);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = tid >> 6;  // 0 .. 4*KS-1
   const int lane = tid & 63;
-  const int c = lane & 31;
-  const int hf = lane >> 5;
+  const int qg = wave & 3;    // query group: rows 32*qg .. +31 of the tile
+  const int kh = wave >> 2;   // key half (KS = 2)
+  const int c = lane & 31;    // query column of the S^T / O^T tiles
+  const int hf = lane >> 5;   // half-wave
 
-  const float* qh = p.q + (int64_t)head * p.q_head_stride;
-  const float* kh = p.k + (int64_t)head * p.kv_head_stride;
-  const float* vh = p.v + (int64_t)head * p.kv_head_stride;
-  float* oh = p.o + (int64_t)head * p.q_head_stride;
+  const T* qh = p.q + (int64_t)head * p.q_head_stride;
+  const T* kh_ptr = p.k + (int64_t)head * p.kv_head_stride;
+  const T* vh_ptr = p.v + (int64_t)head * p.kv_head_stride;
+  T* oh = p.o + (int64_t)head * p.q_head_stride;
 
   const int kv_len = p.kv_len;
-  const int shift = kv_len - p.S_q;
+  const int shift = kv_len - p.S_q;  // absolute position of query row r is r + shift
   const int kv_end = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
   const int n_tiles = (kv_end + BN - 1) / BN;
+  const int n_super = (n_tiles + KS - 1) / KS;
 
-  const int wrow0 = row0 + wave * 32;
+  // This wave's query rows and their positions.
+  const int wrow0 = row0 + qg * 32;
   const int qrow = wrow0 + c;
   const bool wave_live = wrow0 < row1;
-  const int wlast = min(wrow0 + 31, row1 - 1);
+  const int wlast = min(wrow0 + 31, row1 - 1);  // last valid row of the wave
   const int pos = qrow + shift;
   const int pos_first = wrow0 + shift;
   const int pos_last = wlast + shift;
 
-  // Q^T operand: k-step t uses d = 32*hf + t, so the lane holds Q[qrow][32hf .. 32hf+31].
-  float qv[32];
+  // Q operand (B operand of S^T = K Q^T), resident for the whole key loop.
+  // 16-bit: k-step t holds Q[qrow][32hf + 8t .. +7]; fp32: k-step t holds Q[qrow][32hf + t].
+  typename std::conditional<F32, float[32], typename Half16<typename std::conditional<F32, __bf16, T>::type>::vec8[4]>::type qop;
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * HEAD_DIM + 32 * hf);
+    constexpr int NQ = F32 ? 8 : 4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NQ; ++j) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (qrow < row1) x = src[j];
       x ^= p.q_flip;
-      qv[4 * j + 0] = __uint_as_float(x[0]);
-      qv[4 * j + 1] = __uint_as_float(x[1]);
-      qv[4 * j + 2] = __uint_as_float(x[2]);
-      qv[4 * j + 3] = __uint_as_float(x[3]);
+      if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qop[4 * j + e] = __uint_as_float(x[e]);
+      } else {
+        qop[j] = __builtin_bit_cast(typename std::remove_reference<decltype(qop[0])>::type, x);
+      }
     }
   }
 
-  // Tile copies: wave w, copy i < 4 fills tile rows 4(4i + w) .. +3 (one
-  // 256-byte row per 16 lanes); lane l lands in row + l/16, physical chunk
-  // l % 16 and fetches the logical chunk the row's swizzle maps there.
-  int krow[4], kch[4], vch[4], dst[4];
+  // Tile copies: copy i of wave w fills stage rows RPC*(4*KS*i + w) .. +RPC-1
+  // of K and of V; lane l lands in row + l/LPR, physical chunk l%LPR and
+  // fetches the logical chunk the row's swizzle maps there.  Rows past the
+  // cache end re-read row kv_len - 1 (finite data; those keys are masked).
+  int crow[NCP], kch[NCP], vch[NCP], cdst[NCP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (4 * i + wave) + (lane >> 4);
-    krow[i] = row;
-    kch[i] = (lane & 15) ^ (row & 15);
-    vch[i] = lane & 15;
-    dst[i] = 4 * (4 * i + wave) * 256;
+  for (int i = 0; i < NCP; ++i) {
+    const int row = RPC * (4 * KS * i + wave) + lane / LPR;
+    const int ph = lane % LPR;
+    crow[i] = row;
+    if constexpr (F32) {
+      kch[i] = ph ^ (row & 15);
+      vch[i] = ph;
+    } else {
+      kch[i] = ph ^ ((row & 7) ^ ((row >> 3) & 1));
+      vch[i] = ph ^ ((row & 3) << 1);
+    }
+    cdst[i] = RPC * (4 * KS * i + wave) * ROWB;
   }
-  auto issue = [&](char* st, int kv0) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  auto issue = [&](char* st, int super) {
+    const int kv0 = super * KS * BN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = min(kv0 + krow[i], kv_len - 1);
-      dma16(kh + r * HEAD_DIM + kch[i] * 4, st + dst[i]);
-      dma16(vh + r * HEAD_DIM + vch[i] * 4, st + 64 * 256 + dst[i]);
+    for (int i = 0; i < NCP; ++i) {
+      const int64_t r = min(kv0 + crow[i], kv_len - 1);
+      dma16(kh_ptr + r * HEAD_DIM + kch[i] * EPC, st + cdst[i]);
+      dma16(vh_ptr + r * HEAD_DIM + vch[i] * EPC, st + KS * TILE + cdst[i]);
     }
   };
 
@@ -649,71 +561,164 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_k32(Params<float> p) {
     acc[0][r] = 0.f;
     acc[1][r] = 0.f;
   }
-  float m = -INFINITY;
-  float l = 0.f;
+  float m = -INFINITY;  // exponent offset (log2 units), per row
+  float l = 0.f;        // this lane's share of the row sum
   const float cc = p.c;
 
-  auto compute = [&](const char* st, int j) {
-    const int kv0 = j * BN;
+  auto compute = [&](const char* st, int super) {
+    const int t = super * KS + kh;
+    if (t >= n_tiles) return;
+    const int kv0 = t * BN;
+    // Which 32-key blocks can some row of this wave see, and does any key of
+    // the tile need masking (cache end, or past the first row's position)?
     const bool blk0 = wave_live && (!CAUSAL || kv0 <= pos_last);
     if (!blk0) return;
     const bool blk1 = kv0 + 32 < kv_len && (!CAUSAL || kv0 + 32 <= pos_last);
     const int last_key = kv0 + (blk1 ? 63 : 31);
     const bool need_mask = last_key >= kv_len || (CAUSAL && last_key > pos_first);
-    const char* ks = st;
-    const char* vs = st + 64 * 256;
-    if (blk1) {
-      if (need_mask)
-        tile32<true, true, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
-      else
-        tile32<true, false, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
+    const char* ks = st + kh * TILE;
+    const char* vs = st + KS * TILE + kh * TILE;
+    if constexpr (F32) {
+      if (blk1) {
+        if (need_mask)
+          tile32<true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+        else
+          tile32<true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      } else {
+        if (need_mask)
+          tile32<false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+        else
+          tile32<false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      }
     } else {
-      if (need_mask)
-        tile32<false, true, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
-      else
-        tile32<false, false, CAUSAL>(ks, vs, qv, acc, m, l, cc, kv0, kv_len, pos, lane);
+      if (blk1) {
+        if (need_mask)
+          tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+        else
+          tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      } else {
+        if (need_mask)
+          tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+        else
+          tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      }
     }
   };
-  // Same three-stage schedule as the 16-bit kernel; 8 copies per tile per wave.
-  auto step = [&](const char* cur, char* nxt, int j) {
-    if (j + 1 < n_tiles)
-      wait_vmem<8>();
-    else
+
+  if constexpr (NS == 3) {
+    // Stage j % 3 holds super-tile j.  At step j super-tiles j and j+1 may be
+    // in flight: wait for j, barrier (everyone is done with j-1), start j+2
+    // into j-1's stage, compute j.
+    auto step = [&](const char* cur, char* nxt, int j) {
+      if (j + 1 < n_super)
+        wait_vmem<2 * NCP>();
+      else
+        wait_vmem<0>();
+      barrier_keep_dma();
+      if (j + 2 < n_super) issue(nxt, j + 2);
+      compute(cur, j);
+    };
+    if (n_super > 0) issue(st0, 0);
+    if (n_super > 1) issue(st1, 1);
+    for (int j = 0; j < n_super; j += 3) {
+      step(st0, st2, j);
+      if (j + 1 >= n_super) break;
+      step(st1, st0, j + 1);
+      if (j + 2 >= n_super) break;
+      step(st2, st1, j + 2);
+    }
+  } else {
+    // Two stages: wait for j, barrier, start j+1 into j-1's stage, compute j.
+    auto step = [&](const char* cur, char* nxt, int j) {
       wait_vmem<0>();
-    barrier_keep_dma();
-    if (j + 2 < n_tiles) issue(nxt, (j + 2) * BN);
-    compute(cur, j);
-  };
-  if (n_tiles > 0) issue(st0, 0);
-  if (n_tiles > 1) issue(st1, BN);
-  for (int j = 0; j < n_tiles; j += 3) {
-    step(st0, st2, j);
-    if (j + 1 >= n_tiles) break;
-    step(st1, st0, j + 1);
-    if (j + 2 >= n_tiles) break;
-    step(st2, st1, j + 2);
+      barrier_keep_dma();
+      if (j + 1 < n_super) issue(nxt, j + 1);
+      compute(cur, j);
+    };
+    if (n_super > 0) issue(st0, 0);
+    for (int j = 0; j < n_super; j += 2) {
+      step(st0, st1, j);
+      if (j + 1 >= n_super) break;
+      step(st1, st0, j + 1);
+    }
   }
 
+  if constexpr (KS == 2) {
+    // Merge the odd-tile waves' state into the even-tile waves (same query
+    // rows, same register layout): with offsets m0, m1 and mt = max(m0, m1),
+    // acc = acc0 2^(m0-mt) + acc1 2^(m1-mt), likewise l.  Stage 0 holds acc
+    // as 16-byte quads [group][quad][lane]; stage 1 holds (m, l) per lane.
+    // Every copy has completed (the last step waited for all of them).
+    u32x4* racc = reinterpret_cast<u32x4*>(st0);
+    u32x2* rml = reinterpret_cast<u32x2*>(st1);
+    barrier_keep_dma();
+    if (kh == 1) {
+#pragma unroll
+      for (int qd = 0; qd < 8; ++qd) {
+        const f32x16& a = acc[qd >> 2];
+        const int r = 4 * (qd & 3);
+        const u32x4 w = {__float_as_uint(a[r]), __float_as_uint(a[r + 1]), __float_as_uint(a[r + 2]),
+                         __float_as_uint(a[r + 3])};
+        racc[(qg * 8 + qd) * 64 + lane] = w;
+      }
+      const u32x2 ml = {__float_as_uint(m), __float_as_uint(l)};
+      rml[qg * 64 + lane] = ml;
+    }
+    barrier_keep_dma();
+    if (kh == 1) return;
+    const u32x2 ml1 = rml[qg * 64 + lane];
+    const float m1 = __uint_as_float(ml1[0]);
+    const float l1 = __uint_as_float(ml1[1]);
+    const float mt = fmaxf(m, m1);
+    const float a0 = (m == -INFINITY) ? 0.f : fast_exp2(m - mt);
+    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mt);
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int qd = 0; qd < 8; ++qd) {
+      const u32x4 w = racc[(qg * 8 + qd) * 64 + lane];
+      f32x16& a = acc[qd >> 2];
+      const int r = 4 * (qd & 3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[r + e] = a[r + e] * a0 + __uint_as_float(w[e]) * a1;
+    }
+  }
+
+  // Epilogue: O = acc / l, rounded to T, for the rows this wave owns.
   const float lt = l + other_half(l);
   const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
   if (qrow < row1) {
-    // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
-    // 4g .. 4g+3 of both accumulators cover columns 16g + 8hf .. +7.
-    float* orow = oh + (int64_t)qrow * HEAD_DIM;
+    T* orow = oh + (int64_t)qrow * HEAD_DIM;
+    if constexpr (F32) {
+      // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
+      // 4g .. 4g+3 of both accumulators cover columns 16g + 8hf .. +7.
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d = 16 * gq + 8 * hf;
-      u32x4 w0, w1;
-      w0[0] = __float_as_uint(acc[0][4 * gq] * inv);
-      w0[1] = __float_as_uint(acc[1][4 * gq] * inv);
-      w0[2] = __float_as_uint(acc[0][4 * gq + 1] * inv);
-      w0[3] = __float_as_uint(acc[1][4 * gq + 1] * inv);
-      w1[0] = __float_as_uint(acc[0][4 * gq + 2] * inv);
-      w1[1] = __float_as_uint(acc[1][4 * gq + 2] * inv);
-      w1[2] = __float_as_uint(acc[0][4 * gq + 3] * inv);
-      w1[3] = __float_as_uint(acc[1][4 * gq + 3] * inv);
-      *reinterpret_cast<u32x4*>(orow + d) = w0;
-      *reinterpret_cast<u32x4*>(orow + d + 4) = w1;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 16 * gq + 8 * hf;
+        u32x4 w0, w1;
+        w0[0] = __float_as_uint(acc[0][4 * gq] * inv);
+        w0[1] = __float_as_uint(acc[1][4 * gq] * inv);
+        w0[2] = __float_as_uint(acc[0][4 * gq + 1] * inv);
+        w0[3] = __float_as_uint(acc[1][4 * gq + 1] * inv);
+        w1[0] = __float_as_uint(acc[0][4 * gq + 2] * inv);
+        w1[1] = __float_as_uint(acc[1][4 * gq + 2] * inv);
+        w1[2] = __float_as_uint(acc[0][4 * gq + 3] * inv);
+        w1[3] = __float_as_uint(acc[1][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x4*>(orow + d) = w0;
+        *reinterpret_cast<u32x4*>(orow + d + 4) = w1;
+      }
+    } else {
+      typedef Half16<T> H;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * dt + 8 * gq + 4 * hf;
+          u32x2 w;
+          w[0] = H::pack2(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv);
+          w[1] = H::pack2(acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      }
     }
   }
 }
@@ -721,20 +726,25 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_k32(Params<float> p) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-std::atomic<int> g_arch_ok[64];  // 0 unknown, 1 gfx950, 2 other
+// Per-device cache: 0 unknown, -1 not gfx950, else the compute-unit count.
+std::atomic<int> g_dev_cu[64];
 
-int check_device() {
+int check_device(int* n_cu) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_E_DEVICE;
   if (dev < 64) {
-    const int s = g_arch_ok[dev].load(std::memory_order_relaxed);
-    if (s == 1) return ATTN_OK;
-    if (s == 2) return ATTN_E_DEVICE;
+    const int s = g_dev_cu[dev].load(std::memory_order_relaxed);
+    if (s > 0) {
+      *n_cu = s;
+      return ATTN_OK;
+    }
+    if (s < 0) return ATTN_E_DEVICE;
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_E_DEVICE;
-  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.multiProcessorCount > 0;
+  if (dev < 64) g_dev_cu[dev].store(ok ? prop.multiProcessorCount : -1, std::memory_order_relaxed);
+  *n_cu = prop.multiProcessorCount;
   return ok ? ATTN_OK : ATTN_E_DEVICE;
 }
 
@@ -748,7 +758,9 @@ int validate(const void* q, const void* k, const void* v, void* o, int B, int H,
   if (!q || !k || !v || !o) return ATTN_E_NULL;
   if (B < 1 || H < 1 || S_q < 1 || S_kv < 1 || D_h != HEAD_DIM) return ATTN_E_SHAPE;
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
-  if (!std::isfinite(scale)) return ATTN_E_SCALE;
+  uint32_t sbits;
+  std::memcpy(&sbits, &scale, 4);
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_E_SCALE;  // NaN or infinity
   if (chunk < 1 || kv_len < 1 || kv_len > S_kv) return ATTN_E_CHUNK;
   if (causal && S_q > kv_len) return ATTN_E_CAUSAL;
   // sizes: elements and bytes fit in int64; the grid fits in 2^31 - 1
@@ -769,8 +781,9 @@ int validate(const void* q, const void* k, const void* v, void* o, int B, int H,
   return ATTN_OK;
 }
 
-Sched make_sched(int B, int H, int S_q, int chunk) {
+Sched make_sched(int B, int H, int S_q, int chunk, int kv_len, int causal) {
   Sched s;
+  s.tile_major = causal && kv_len <= TILE_MAJOR_MAX_KV;
   s.S_q = S_q;
   s.chunk = std::min(chunk, S_q);
   s.n_win = (S_q + s.chunk - 1) / s.chunk;
@@ -783,9 +796,17 @@ Sched make_sched(int B, int H, int S_q, int chunk) {
   return s;
 }
 
+template <typename T, int KS>
+void launch_kernel(const Params<T>& p, int grid, int causal, hipStream_t stream) {
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+}
+
 template <typename T>
 int launch_typed(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
-                 int causal, float scale, hipStream_t stream, int chunk, int kv_len) {
+                 int causal, float scale, hipStream_t stream, int chunk, int kv_len, int n_cu) {
   Params<T> p;
   p.q = static_cast<const T*>(q);
   p.k = static_cast<const T*>(k);
@@ -800,19 +821,17 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   // exp2(~1e-27) = 1 exactly in fp32.
   p.c = (float)std::max(std::fabs((double)scale) * 1.4426950408889634, 1e-30);
   p.q_flip = (scale < 0.f) ? (sizeof(T) == 4 ? 0x80000000u : 0x80008000u) : 0u;
-  p.s = make_sched(B, H, S_q, chunk);
+  p.s = make_sched(B, H, S_q, chunk, kv_len, causal);
   const int grid = p.s.groups * p.s.heads * (p.s.tl + (p.s.n_win - 1) * p.s.tf);
-  if constexpr (sizeof(T) == 4) {
-    if (causal)
-      hipLaunchKernelGGL(attn_fwd_k32<true>, dim3(grid), dim3(NTHREADS), 0, stream, p);
-    else
-      hipLaunchKernelGGL(attn_fwd_k32<false>, dim3(grid), dim3(NTHREADS), 0, stream, p);
-  } else {
-    if (causal)
-      hipLaunchKernelGGL((attn_fwd_k16<T, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_k16<T, false>), dim3(grid), dim3(NTHREADS), 0, stream, p);
-  }
+  // Few 128-row query tiles (at most two per CU): split each tile's key range
+  // between two wave groups so every SIMD runs two waves on half the key
+  // chain.  The choice depends on B, H and S_q only, never on the window
+  // size, so chunked and unchunked calls sum in the same order.
+  const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
+  if (tiles <= 2 * (int64_t)n_cu)
+    launch_kernel<T, 2>(p, grid, causal, stream);
+  else
+    launch_kernel<T, 1>(p, grid, causal, stream);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
@@ -823,16 +842,17 @@ extern "C" int attn_fwd_chunked(const void* q, const void* k, const void* v, voi
                                 int chunk, int kv_len) {
   const int st = validate(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, chunk, kv_len);
   if (st != ATTN_OK) return st;
-  const int dv = check_device();
+  int n_cu = 0;
+  const int dv = check_device(&n_cu);
   if (dv != ATTN_OK) return dv;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case ATTN_F32:
-      return launch_typed<float>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len);
+      return launch_typed<float>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len, n_cu);
     case ATTN_F16:
-      return launch_typed<_Float16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len);
+      return launch_typed<_Float16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len, n_cu);
     default:
-      return launch_typed<__bf16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len);
+      return launch_typed<__bf16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, chunk, kv_len, n_cu);
   }
 }
 
@@ -841,23 +861,24 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, in
   return attn_fwd_chunked(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, stream, S_q, S_kv);
 }
 
-extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int* grid) {
-  if (B < 1 || H < 1 || S_q < 1 || chunk < 1 || !grid) return ATTN_E_SHAPE;
+extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int* grid) {
+  if (B < 1 || H < 1 || S_q < 1 || chunk < 1 || kv_len < 1 || !grid) return ATTN_E_SHAPE;
   const int64_t bh = (int64_t)B * H;
   const int64_t n_win = ((int64_t)S_q + chunk - 1) / chunk;
   const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + BM - 1) / BM);
   if (bh > (int64_t)INT32_MAX || tiles * bh > (int64_t)INT32_MAX) return ATTN_E_SHAPE;
-  const Sched s = make_sched(B, H, S_q, chunk);
+  const Sched s = make_sched(B, H, S_q, chunk, kv_len, causal);
   *grid = s.groups * s.heads * (s.tl + (s.n_win - 1) * s.tf);
   return ATTN_OK;
 }
 
-extern "C" int attn_sched_tile(int B, int H, int S_q, int chunk, int block, int* head, int* row0, int* row1) {
+extern "C" int attn_sched_tile(int B, int H, int S_q, int chunk, int kv_len, int causal, int block, int* head,
+                               int* row0, int* row1) {
   int grid = 0;
-  const int st = attn_sched_grid(B, H, S_q, chunk, &grid);
+  const int st = attn_sched_grid(B, H, S_q, chunk, kv_len, causal, &grid);
   if (st != ATTN_OK) return st;
   if (block < 0 || block >= grid || !head || !row0 || !row1) return ATTN_E_SHAPE;
-  decode_tile(make_sched(B, H, S_q, chunk), block, *head, *row0, *row1);
+  decode_tile(make_sched(B, H, S_q, chunk, kv_len, causal), block, *head, *row0, *row1);
   return ATTN_OK;
 }
 
