@@ -63,12 +63,18 @@ def attn_strerror(status: int) -> str:
     return lib.attn_strerror(int(status)).decode()
 
 
+_codes = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
-    if t.dtype not in codes:
+    global _codes
+    if _codes is None:
+        torch = _t()
+        _codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    c = _codes.get(t.dtype)
+    if c is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return c
 
 
 def _check(q, k, v):
@@ -89,17 +95,43 @@ def _check(q, k, v):
     return B, H, S_q, k.shape[2], D
 
 
+_torch = None
+_raw_stream = None
+
+
+def _t():
+    """torch, imported on first use (the library itself does not need it)."""
+    global _torch, _raw_stream
+    if _torch is None:
+        import torch
+        _torch = torch
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    return _torch
+
+
 def _stream_ptr(device, stream):
-    import torch
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    torch = _t()
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _call(fn, device, *args):
+    """Call into the library with `device` current (switching only if needed)."""
+    torch = _t()
+    if device.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
 
 
 def attn_fwd_chunked(q, k, v, chunk: int, kv_len: int | None = None, causal: bool = False,
                      scale: float | None = None, out=None, stream=None):
     """Chunked/streaming forward: query windows of `chunk` rows against the first
     kv_len rows of the K/V cache (see attn_fwd_chunked in include/attn.h)."""
-    import torch
+    torch = _t()
     B, H, S_q, S_kv, D = _check(q, k, v)
     if kv_len is None:
         kv_len = S_kv
@@ -108,10 +140,10 @@ def attn_fwd_chunked(q, k, v, chunk: int, kv_len: int | None = None, causal: boo
     o = torch.empty_like(q) if out is None else out
     if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
-    with torch.cuda.device(q.device):
-        st = lib.attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                  B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
-                                  _dtype_code(q), _stream_ptr(q.device, stream), int(chunk), int(kv_len))
+    dev = q.device
+    st = _call(lib.attn_fwd_chunked, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+               B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
+               _dtype_code(q), _stream_ptr(dev, stream), int(chunk), int(kv_len))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o
@@ -119,17 +151,17 @@ def attn_fwd_chunked(q, k, v, chunk: int, kv_len: int | None = None, causal: boo
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, stream=None):
     """O = softmax(Q K^T * scale [+ causal mask]) V (see attn_fwd in include/attn.h)."""
-    import torch
+    torch = _t()
     B, H, S_q, S_kv, D = _check(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
     if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
-    with torch.cuda.device(q.device):
-        st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                          B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
-                          _dtype_code(q), _stream_ptr(q.device, stream))
+    dev = q.device
+    st = _call(lib.attn_fwd, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+               B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
+               _dtype_code(q), _stream_ptr(dev, stream))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o
