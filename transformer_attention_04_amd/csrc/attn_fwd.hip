@@ -27,12 +27,21 @@
 //
 // Softmax numerics: scores, m, l and the accumulator are fp32.  exp(x) is
 // evaluated as exp2(x * log2 e) with log2 e folded into the score scale (one
-// FMA per score).  The row maximum used as the exponent offset is only raised
-// when a new block exceeds it by more than 2^8 ("lazy" rescaling); this keeps
-// every probability <= 256, changes nothing in exact arithmetic (the offset
-// cancels between numerator and denominator), and skips the accumulator
-// rescale on most blocks.  Probabilities are rounded to bf16/fp16 only as the
-// MFMA operand of the P V product; l sums the fp32 values.
+// FMA per score).  The exponent offset m of a row is any value at which the
+// probabilities exp2(s - m) stay in range; in exact arithmetic it cancels
+// between numerator and denominator.  It is set from the row maximum until
+// every row of the wave has one, and afterwards left alone: a block's
+// probabilities are taken with the current offset and only if some lane's sum
+// over the block exceeds 2^15 are the block's scores recomputed, their maximum taken
+// and the offset raised to it when that maximum exceeds it by more than 2^8
+// (then acc and l are rescaled by exp2(m_old - m_new)).  Steady-state blocks
+// therefore need neither the row maximum nor a rescale, and every probability
+// fed to the P V product is <= 2^15, inside the fp16 range.  Probabilities are
+// rounded to bf16/fp16 as the MFMA operand of the P V product and l sums the
+// same rounded values (so O is an exact weighted mean of the V rows with those
+// weights).  fp32 inputs keep fp32 probabilities and take the maximum on every
+// block (their fp32 MFMAs dominate; the lazy 2^8 rule still skips most
+// rescales).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -59,7 +68,8 @@ constexpr int HEAD_DIM = 64;
 constexpr int BM = 128;        // query rows per workgroup
 constexpr int BN = 64;         // keys per iteration
 constexpr int NTHREADS = 256;  // 4 wavefronts of 64
-constexpr float LAZY_TH = 8.0f;  // log2 headroom before the offset is raised
+constexpr float LAZY_TH = 8.0f;       // log2 headroom before the offset is raised
+constexpr float P_LIMIT = 32768.0f;  // largest per-lane block sum taken without a max
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -240,6 +250,11 @@ struct Half16<__bf16> {
   __device__ static __forceinline__ unsigned pack2(float x, float y) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
   }
+  // acc + w.x + w.y for a packed pair (v_dot2c_f32_bf16 against ones)
+  __device__ static __forceinline__ float add_pair(unsigned w, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
 };
 
 template <>
@@ -250,6 +265,11 @@ struct Half16<_Float16> {
   }
   __device__ static __forceinline__ unsigned pack2(float x, float y) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, f16x2));
+  }
+  // acc + w.x + w.y for a packed pair (v_dot2c_f32_f16 against ones)
+  __device__ static __forceinline__ float add_pair(unsigned w, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
   }
 };
 
@@ -266,32 +286,73 @@ __device__ __forceinline__ int v16_off(int row, int c16) {
   return row * 128 + ((c16 ^ ((row & 3) << 1)) << 4);
 }
 
+// Probabilities of one tile for the 16-bit path: P = exp2(s*c - moff) in fp32,
+// RNE-packed to 16 bits in the B-operand layout of the P V product (pw[kb][u]
+// word q holds keys 8u + 2q, 8u + 2q + 1 of block kb, k-slots 8hf + 2q, +1).
+// Returns this lane's sum of the packed (rounded) values.
+template <typename T, int NB>
+__device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, const float moff,
+                                         u32x4 (&pw)[NB][2]) {
+  typedef Half16<T> H;
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 8 * u + 2 * q;
+        const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
+        const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
+        const unsigned w = H::pack2(e0, e1);
+        pw[kb][u][q] = w;
+        ls[q] = H::add_pair(w, ls[q]);
+      }
+  return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
 // One wave's work on one 64-key tile: S^T = K Q^T on MFMA, online-softmax
 // update, O^T += V^T P^T on MFMA.  TWO: the tile's second 32-key block is
 // visible to some row of this wave (false only on causal diagonal tiles and
 // at the cache end).  MASK: some key of the tile is invisible to some row.
+// primed (wave-uniform): every row of the wave has a finite offset m.
 template <typename T, bool TWO, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typename Half16<T>::vec8 (&qop)[4],
-                                       f32x16 (&acc)[2], float& m, float& l, const float cc,
+                                       f32x16 (&acc)[2], float& m, float& l, bool& primed, const float cc,
                                        const int kv0, const int kv_len, const int pos, const int lane) {
   typedef Half16<T> H;
   typedef typename H::vec8 vec8;
   constexpr int NB = TWO ? 2 : 1;
   const int c = lane & 31, hf = lane >> 5;
 
-  // S^T = K Q^T; k-step t: lane holds K[32kb + c][32hf + 8t .. +7].
-  f32x16 s[NB];
+  // S^T = K Q^T; k-step t: lane holds K[32kb + c][32hf + 8t .. +7].  Keys
+  // this lane's row cannot see get -inf (exp2(-inf) = 0); only diagonal and
+  // cache-end tiles carry the mask.
+  auto scores = [&](f32x16 (&s)[NB]) {
 #pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      const vec8 a = *reinterpret_cast<const vec8*>(ks + k16_off(32 * kb + c, 4 * hf + t));
-      s[kb] = H::mfma(a, qop[t], s[kb]);
+      for (int kb = 0; kb < NB; ++kb) {
+        const vec8 a = *reinterpret_cast<const vec8*>(ks + k16_off(32 * kb + c, 4 * hf + t));
+        s[kb] = H::mfma(a, qop[t], s[kb]);
+      }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = key < kv_len && (!CAUSAL || key <= pos);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
     }
+  };
+  f32x16 s[NB];
+  scores(s);
 
   // V^T operands, read transposed from the [key][d] tile before the softmax
   // so their latency overlaps it.  Operand (kb, u, dt), k-slot 8hf + e, holds
@@ -317,42 +378,37 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
         }
   }
 
-  // Mask only diagonal / cache-end tiles: -inf scores give exp2(-inf) = 0.
-  if constexpr (MASK) {
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const bool vis = key < kv_len && (!CAUSAL || key <= pos);
-        s[kb][r] = vis ? s[kb][r] : -INFINITY;
-      }
+  // Steady state: take the probabilities at the current offset.  Before the
+  // offsets are set, or if any lane's block sum is out of range, go through
+  // the maximum.  One call site keeps a single rescale point for acc.
+  u32x4 pw[NB][2];
+  float ts = 0.f;
+  bool need_max = !primed;
+  if (primed) {
+    ts = probs16<T, NB>(s, cc, m, pw);
+    need_max = __any(ts > P_LIMIT);
   }
+  if (need_max) {
+    // s is dead past this point either way: re-read K and recompute it here
+    // so no score register lives across the branch.
+    asm volatile("" ::: "memory");
+    f32x16 s2[NB];
+    scores(s2);
+    const float moff = online_offset<NB>(s2, acc, m, l, cc);  // may rescale acc and l
+    ts = probs16<T, NB>(s2, cc, moff, pw);
+    primed = __all(m != -INFINITY);
+  }
+  l += ts;
 
-  const float moff = online_offset<NB>(s, acc, m, l, cc);
-
-  // P = exp2(s*c - m) in fp32 (row sum from the fp32 values), RNE-packed to
-  // 16 bits straight into the B operand of step (kb, u): k-slot 8hf + e holds
-  // P[kb][8u + e].  O^T += V^T P^T.
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
+  // O^T += V^T P^T: step (kb, u) contracts keys 32kb + 16u .. +15.
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      u32x4 bw;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 8 * u + 2 * q;
-        const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
-        const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
-        ls[q] += e0 + e1;
-        bw[q] = H::pack2(e0, e1);
-      }
-      const vec8 b = __builtin_bit_cast(vec8, bw);
+      const vec8 b = __builtin_bit_cast(vec8, pw[kb][u]);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) acc[dt] = H::mfma(va[kb][u][dt], b, acc[dt]);
     }
-  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -368,6 +424,22 @@ __device__ __forceinline__ int k32_off(int row, int c16) {
 // 32 lanes (lanes 0-31 row R, lanes 32-63 row R + 4), which is conflict-free
 // as is, and fixed row offsets become immediate address offsets.
 
+// fp32 probabilities of one tile, in place: s <- exp2(s*c - moff).  Returns
+// this lane's sum of them.
+template <int NB>
+__device__ __forceinline__ float probs32(f32x16 (&s)[NB], const float cc, const float moff) {
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
+      ls[r & 3] += e;
+      s[kb][r] = e;
+    }
+  return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
 // One wave's work on one 64-key fp32 tile (see tile16 for TWO and MASK).
 // The two O^T accumulators hold interleaved columns: acc[dt] row i is
 // d = 2i + dt, so one 8-byte read V[key][2c .. 2c+1] feeds both P V MFMAs.
@@ -379,23 +451,36 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
   const int c = lane & 31, hf = lane >> 5;
 
   // S^T = K Q^T: k-step t contracts d = 32hf + t; lane reads K[32kb + c][32hf .. +31]
-  // as eight 16-byte chunks, each feeding four MFMAs.
-  f32x16 s[NB];
+  // as eight 16-byte chunks, each feeding four MFMAs.  Masked keys get -inf.
+  auto scores = [&](f32x16 (&s)[NB]) {
 #pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x4 ka[NB];
+    for (int j = 0; j < 8; ++j) {
+      u32x4 ka[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(ks + k32_off(32 * kb + c, 8 * hf + j));
+      for (int kb = 0; kb < NB; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(ks + k32_off(32 * kb + c, 8 * hf + j));
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ka[kb][e]), qv[4 * j + e], s[kb], 0, 0, 0);
+    }
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ka[kb][e]), qv[4 * j + e], s[kb], 0, 0, 0);
-  }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = key < kv_len && (!CAUSAL || key <= pos);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
+    }
+  };
+  f32x16 s[NB];
+  scores(s);
 
   // V operands of block 0, read ahead of the softmax: step r of block kb
   // contracts keys 32kb + 8(r/4) + 4hf + r%4 (k-slot hf), lane (c, hf) needs
@@ -406,29 +491,10 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
   for (int r = 0; r < 16; ++r)
     va[0][r] = *reinterpret_cast<const f32x2*>(vlane + (8 * (r >> 2) + (r & 3)) * 256);
 
-  if constexpr (MASK) {
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const bool vis = key < kv_len && (!CAUSAL || key <= pos);
-        s[kb][r] = vis ? s[kb][r] : -INFINITY;
-      }
-  }
-
-  const float moff = online_offset<NB>(s, acc, m, l, cc);
-
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
-      ls[r & 3] += e;
-      s[kb][r] = e;
-    }
-  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  // fp32 tiles are bound by the fp32 MFMA rate: the row maximum costs less
+  // than the register traffic of the max-free path, so every tile takes it.
+  const float moff = online_offset<NB>(s, acc, m, l, cc);  // may rescale acc and l
+  l += probs32<NB>(s, cc, moff);
 
   // O^T += V^T P^T, one key pair per MFMA: k-slot hf of step r is this lane's
   // probability s[kb][r].  Block 1's operands are read during block 0's MFMAs.
@@ -478,7 +544,11 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   decode_tile(p.s, blockIdx.x, head, row0, row1);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;  // 0 .. 4*KS-1
+  // 0 .. 4*KS-1.  Deliberately not made compiler-uniform (readfirstlane):
+  // with scalar branches the per-tile variants below join in ways that make
+  // the register allocator copy the accumulators in and out on every tile;
+  // as exec-masked branches they stay in place.
+  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int qg = wave & 3;    // query group: rows 32*qg .. +31 of the tile
   const int kh = wave >> 2;   // key half (KS = 2)
@@ -563,6 +633,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   }
   float m = -INFINITY;  // exponent offset (log2 units), per row
   float l = 0.f;        // this lane's share of the row sum
+  bool primed = false;  // every row of this wave has a finite offset (wave-uniform)
   const float cc = p.c;
 
   auto compute = [&](const char* st, int super) {
@@ -593,14 +664,14 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     } else {
       if (blk1) {
         if (need_mask)
-          tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
         else
-          tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
       } else {
         if (need_mask)
-          tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
         else
-          tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
       }
     }
   };
