@@ -65,7 +65,7 @@ enum attn_dtype {
 enum attn_status {
     ATTN_OK = 0,
     ATTN_E_NULL = 1,     /* q, k, v or o is NULL */
-    ATTN_E_SHAPE = 2,    /* B, H, S_q or S_kv < 1; D_h != 64; sizes overflow */
+    ATTN_E_SHAPE = 2,    /* B, H, S_q or S_kv < 1; D_h != 64; sizes overflow; one head of K/V >= 4 GiB */
     ATTN_E_DTYPE = 3,    /* dtype not an attn_dtype value */
     ATTN_E_SCALE = 4,    /* scale is NaN or infinite */
     ATTN_E_CAUSAL = 5,   /* causal with S_q > kv_len (a row would see no key) */

@@ -66,6 +66,8 @@ def call(**kw):
     (dict(B=0), 2), (dict(H=-1), 2), (dict(S_q=0), 2), (dict(S_kv=0), 2), (dict(D=32), 2), (dict(D=128), 2),
     (dict(B=1 << 20, H=1 << 12), 2),                      # B*H over 2^31
     (dict(B=1 << 14, H=1 << 14, S_q=1 << 20, S_kv=1 << 20, kv_len=1 << 20), 2),  # element count overflow
+    (dict(S_kv=1 << 24, kv_len=120, dtype=0), 2),        # one fp32 head of K/V is 4 GiB
+    (dict(S_kv=1 << 25, kv_len=120, dtype=2), 2),        # one bf16 head of K/V is 4 GiB
     (dict(dtype=3), 3), (dict(dtype=-1), 3),
     (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=float("-inf")), 4),
     (dict(chunk=0), 6), (dict(kv_len=0), 6), (dict(kv_len=121), 6),
@@ -83,6 +85,16 @@ def test_valid_call_without_gpu_reports_device():
         pytest.skip("a GPU is present")
     assert call() == 9
     assert A.lib.attn_fwd(Q, K, V, O, 2, 3, 100, 120, 64, 0, 0.125, 0, None) == 9
+
+
+def test_largest_head_passes_validation():
+    """One head of K/V just under 4 GiB is accepted (fake addresses far apart)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    q, k, v, o = 1 << 40, 1 << 41, 1 << 42, 1 << 43
+    for dtype, s_kv in ((0, (1 << 24) - 1), (2, (1 << 25) - 1), (1, (1 << 25) - 1)):
+        assert A.lib.attn_fwd_chunked(q, k, v, o, 1, 1, 100, s_kv, 64, 1, 0.125, dtype, None, 64, s_kv) == 9
 
 
 def test_noncausal_allows_more_queries_than_keys():

@@ -162,15 +162,19 @@ __device__ __forceinline__ float max_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's bytes land at lds_base + 16*l; lds_base must be wave-uniform (it
-// goes to M0).  Issued as inline assembly so the compiler does not add its own
-// conservative waits for it before unrelated LDS reads; completion is tracked
-// explicitly with wait_vmem (vmcnt counts these copies, in issue order).
-__device__ __forceinline__ void dma16(const void* gsrc, const char* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)lds_base));
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
+// from sbase + voff: sbase is wave-uniform (an SGPR pair), voff this lane's
+// byte offset (unsigned 32-bit); lane l's bytes land at LDS address m0 + 16*l,
+// m0 wave-uniform.  Issued as inline assembly so the compiler does not add its
+// own conservative waits for it before unrelated LDS reads; completion is
+// tracked explicitly with wait_vmem (vmcnt counts these copies, in issue order).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
+// LDS byte address of a __shared__ location (what M0 takes).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -597,31 +601,49 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
 
   // Tile copies: copy i of wave w fills stage rows RPC*(4*KS*i + w) .. +RPC-1
   // of K and of V; lane l lands in row + l/LPR, physical chunk l%LPR and
-  // fetches the logical chunk the row's swizzle maps there.  Rows past the
-  // cache end re-read row kv_len - 1 (finite data; those keys are masked).
-  int crow[NCP], kch[NCP], vch[NCP], cdst[NCP];
+  // fetches the logical chunk the row's swizzle maps there.  The source is
+  // the head's base advanced to the super-tile (scalar) plus a per-lane
+  // offset that is the same for every super-tile; only a super-tile that
+  // crosses the cache end computes clamped offsets (rows past kv_len - 1
+  // re-read row kv_len - 1: finite data, and those keys are masked).
+  int crow[NCP];
+  uint32_t kcb[NCP], vcb[NCP], kof[NCP], vof[NCP];
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
     const int row = RPC * (4 * KS * i + wave) + lane / LPR;
     const int ph = lane % LPR;
     crow[i] = row;
     if constexpr (F32) {
-      kch[i] = ph ^ (row & 15);
-      vch[i] = ph;
+      kcb[i] = 16 * (ph ^ (row & 15));
+      vcb[i] = 16 * ph;
     } else {
-      kch[i] = ph ^ ((row & 7) ^ ((row >> 3) & 1));
-      vch[i] = ph ^ ((row & 3) << 1);
+      kcb[i] = 16 * (ph ^ ((row & 7) ^ ((row >> 3) & 1)));
+      vcb[i] = 16 * (ph ^ ((row & 3) << 1));
     }
-    cdst[i] = RPC * (4 * KS * i + wave) * ROWB;
+    kof[i] = (uint32_t)row * ROWB + kcb[i];
+    vof[i] = (uint32_t)row * ROWB + vcb[i];
   }
-  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(RPC * wave * ROWB));
+  const char* kbase = reinterpret_cast<const char*>(kh_ptr);
+  const char* vbase = reinterpret_cast<const char*>(vh_ptr);
   auto issue = [&](char* st, int super) {
     const int kv0 = super * KS * BN;
+    const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
+    if (kv0 + KS * BN <= kv_len) {
+      const char* kb = kbase + (int64_t)kv0 * ROWB;
+      const char* vb = vbase + (int64_t)kv0 * ROWB;
 #pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      const int64_t r = min(kv0 + crow[i], kv_len - 1);
-      dma16(kh_ptr + r * HEAD_DIM + kch[i] * EPC, st + cdst[i]);
-      dma16(vh_ptr + r * HEAD_DIM + vch[i] * EPC, st + KS * TILE + cdst[i]);
+      for (int i = 0; i < NCP; ++i) {
+        dma16(kb, kof[i], mk + i * (RPC * 4 * KS * ROWB));
+        dma16(vb, vof[i], mv + i * (RPC * 4 * KS * ROWB));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        const uint32_t rb = (uint32_t)min(kv0 + crow[i], kv_len - 1) * ROWB;
+        dma16(kbase, rb + kcb[i], mk + i * (RPC * 4 * KS * ROWB));
+        dma16(vbase, rb + vcb[i], mv + i * (RPC * 4 * KS * ROWB));
+      }
     }
   };
 
@@ -676,41 +698,77 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     }
   };
 
+  // Tiles every wave of the workgroup sees in full (all keys below the cache
+  // end and, when causal, at or before the workgroup's first row): the
+  // leading super-steps made only of such tiles run a loop without any
+  // visibility or mask logic.
+  int t_full = kv_len / BN;
+  if (CAUSAL) t_full = min(t_full, (row0 + shift + 1) / BN);
+  const int j_full = t_full / KS;
+  auto compute_full = [&](const char* st, int super) {
+    if (!wave_live) return;
+    const char* ks = st + kh * TILE;
+    const char* vs = st + KS * TILE + kh * TILE;
+    const int kv0 = (super * KS + kh) * BN;
+    if constexpr (F32)
+      tile32<true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+    else
+      tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
+  };
+
+  int j = 0;
   if constexpr (NS == 3) {
     // Stage j % 3 holds super-tile j.  At step j super-tiles j and j+1 may be
     // in flight: wait for j, barrier (everyone is done with j-1), start j+2
     // into j-1's stage, compute j.
-    auto step = [&](const char* cur, char* nxt, int j) {
+    auto sync = [&](char* nxt, int j) {
       if (j + 1 < n_super)
         wait_vmem<2 * NCP>();
       else
         wait_vmem<0>();
       barrier_keep_dma();
       if (j + 2 < n_super) issue(nxt, j + 2);
-      compute(cur, j);
     };
     if (n_super > 0) issue(st0, 0);
     if (n_super > 1) issue(st1, 1);
-    for (int j = 0; j < n_super; j += 3) {
-      step(st0, st2, j);
+    for (; j + 3 <= j_full; j += 3) {
+      sync(st2, j);
+      compute_full(st0, j);
+      sync(st0, j + 1);
+      compute_full(st1, j + 1);
+      sync(st1, j + 2);
+      compute_full(st2, j + 2);
+    }
+    for (; j < n_super; j += 3) {
+      sync(st2, j);
+      compute(st0, j);
       if (j + 1 >= n_super) break;
-      step(st1, st0, j + 1);
+      sync(st0, j + 1);
+      compute(st1, j + 1);
       if (j + 2 >= n_super) break;
-      step(st2, st1, j + 2);
+      sync(st1, j + 2);
+      compute(st2, j + 2);
     }
   } else {
     // Two stages: wait for j, barrier, start j+1 into j-1's stage, compute j.
-    auto step = [&](const char* cur, char* nxt, int j) {
+    auto sync = [&](char* nxt, int j) {
       wait_vmem<0>();
       barrier_keep_dma();
       if (j + 1 < n_super) issue(nxt, j + 1);
-      compute(cur, j);
     };
     if (n_super > 0) issue(st0, 0);
-    for (int j = 0; j < n_super; j += 2) {
-      step(st0, st1, j);
+    for (; j + 2 <= j_full; j += 2) {
+      sync(st1, j);
+      compute_full(st0, j);
+      sync(st0, j + 1);
+      compute_full(st1, j + 1);
+    }
+    for (; j < n_super; j += 2) {
+      sync(st1, j);
+      compute(st0, j);
       if (j + 1 >= n_super) break;
-      step(st1, st0, j + 1);
+      sync(st0, j + 1);
+      compute(st1, j + 1);
     }
   }
 
@@ -840,6 +898,8 @@ int validate(const void* q, const void* k, const void* v, void* o, int B, int H,
   const int64_t esz = dtype == ATTN_F32 ? 4 : 2;
   const int64_t lim = INT64_MAX / (HEAD_DIM * esz);
   if ((int64_t)S_q > lim / bh || (int64_t)S_kv > lim / bh) return ATTN_E_SHAPE;
+  // tile copies address one head of K/V with 32-bit byte offsets
+  if ((int64_t)S_kv * HEAD_DIM * esz > (int64_t)UINT32_MAX) return ATTN_E_SHAPE;
   const int64_t n_win = ((int64_t)S_q + chunk - 1) / chunk;
   const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + BM - 1) / BM);
   if (tiles * bh > (int64_t)INT32_MAX) return ATTN_E_SHAPE;
