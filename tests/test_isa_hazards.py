@@ -1,0 +1,49 @@
+"""Checks on the gfx950 assembly of the attention kernels (CPU only: hipcc
+cross-compiles).
+
+The K/V tile copies are `global_load_lds_dwordx4` instructions written as inline
+assembly, which the compiler's hazard recognizer does not look into.  The
+hardware needs one wait state between an SALU write of M0 and an LDS-DMA
+instruction that reads it; without it the copy can take a stale M0 as its LDS
+destination.  The wait is therefore part of the assembly, and this test keeps
+it there: no LDS-DMA instruction may directly follow an instruction whose
+destination is M0.
+"""
+import os
+import subprocess
+
+import pytest
+
+from transformer_attention_04_amd import build as B
+
+
+def _device_asm(tmp_path):
+    if not os.path.exists(B.HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "attn_fwd.s"
+    flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
+    r = subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), B.SRC],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _instructions(asm):
+    for line in asm.splitlines():
+        t = line.strip()
+        if t and not t.startswith((";", ".")) and not t.endswith(":"):
+            yield t
+
+
+def test_no_lds_dma_directly_after_an_m0_write(tmp_path):
+    asm = _device_asm(tmp_path)
+    prev, n, bad = None, 0, []
+    for ins in _instructions(asm):
+        if ins.split()[0].startswith("global_load_lds"):
+            n += 1
+            parts = prev.split(None, 1) if prev else []
+            if len(parts) > 1 and parts[1].split(",")[0].strip() == "m0":
+                bad.append((prev, ins))
+        prev = ins
+    assert n > 0, "no LDS-DMA instruction found"
+    assert not bad, f"{len(bad)} of {n} LDS-DMA instructions directly follow an M0 write, e.g. {bad[0]}"

@@ -168,8 +168,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // m0 wave-uniform.  Issued as inline assembly so the compiler does not add its
 // own conservative waits for it before unrelated LDS reads; completion is
 // tracked explicitly with wait_vmem (vmcnt counts these copies, in issue order).
+// An SALU write of M0 needs one wait state before an LDS-DMA instruction reads
+// it; the compiler's hazard recognizer cannot see inside the assembly, so the
+// s_nop is part of it (without it the copy can take a stale M0 as its LDS
+// destination).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
 // LDS byte address of a __shared__ location (what M0 takes).
