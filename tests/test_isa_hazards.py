@@ -2,12 +2,15 @@
 cross-compiles).
 
 The K/V tile copies are `global_load_lds_dwordx4` instructions written as inline
-assembly, which the compiler's hazard recognizer does not look into.  The
-hardware needs one wait state between an SALU write of M0 and an LDS-DMA
-instruction that reads it; without it the copy can take a stale M0 as its LDS
-destination.  The wait is therefore part of the assembly, and this test keeps
-it there: no LDS-DMA instruction may directly follow an instruction whose
-destination is M0.
+assembly, which the compiler's hazard recognizer does not look into, so their
+operands are restricted to forms that need no wait states from it:
+
+* the global address comes from a VGPR pair (`..., off`), never from an SGPR
+  base: a VMEM read of an SGPR written by a VALU instruction (v_readlane,
+  v_readfirstlane, v_cmp) needs wait states the compiler cannot insert here;
+* the one wait state an SALU write of M0 needs before an LDS-DMA instruction
+  reads it is part of the assembly: no LDS-DMA instruction may directly follow
+  an instruction whose destination is M0.
 """
 import os
 import subprocess
@@ -47,3 +50,11 @@ def test_no_lds_dma_directly_after_an_m0_write(tmp_path):
         prev = ins
     assert n > 0, "no LDS-DMA instruction found"
     assert not bad, f"{len(bad)} of {n} LDS-DMA instructions directly follow an M0 write, e.g. {bad[0]}"
+
+
+def test_lds_dma_addresses_come_from_vgprs(tmp_path):
+    asm = _device_asm(tmp_path)
+    dma = [ins for ins in _instructions(asm) if ins.split()[0].startswith("global_load_lds")]
+    assert dma, "no LDS-DMA instruction found"
+    sgpr_based = [ins for ins in dma if ins.split(None, 1)[1].split(",")[1].strip() != "off"]
+    assert not sgpr_based, f"{len(sgpr_based)} LDS-DMA instructions take an SGPR base, e.g. {sgpr_based[0]}"

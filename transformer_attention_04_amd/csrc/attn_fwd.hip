@@ -163,17 +163,18 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
-// from sbase + voff: sbase is wave-uniform (an SGPR pair), voff this lane's
-// byte offset (unsigned 32-bit); lane l's bytes land at LDS address m0 + 16*l,
-// m0 wave-uniform.  Issued as inline assembly so the compiler does not add its
-// own conservative waits for it before unrelated LDS reads; completion is
-// tracked explicitly with wait_vmem (vmcnt counts these copies, in issue order).
-// An SALU write of M0 needs one wait state before an LDS-DMA instruction reads
-// it; the compiler's hazard recognizer cannot see inside the assembly, so the
-// s_nop is part of it (without it the copy can take a stale M0 as its LDS
-// destination).
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+// from this lane's 64-bit address gsrc (a VGPR pair); lane l's bytes land at
+// LDS address m0 + 16*l, m0 wave-uniform.  Issued as inline assembly so the
+// compiler does not add its own conservative waits for it before unrelated
+// LDS reads; completion is tracked explicitly with wait_vmem (vmcnt counts
+// these copies, in issue order).  The compiler's hazard recognizer cannot see
+// inside the assembly, so the operands are chosen to need no help from it:
+// the address comes from VGPRs (a VMEM read of an SGPR written by a VALU
+// instruction would need wait states the compiler cannot insert here), and
+// the one wait state an SALU write of M0 needs before an LDS-DMA instruction
+// reads it is the s_nop inside the assembly.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
 
 // LDS byte address of a __shared__ location (what M0 takes).
@@ -605,11 +606,11 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
 
   // Tile copies: copy i of wave w fills stage rows RPC*(4*KS*i + w) .. +RPC-1
   // of K and of V; lane l lands in row + l/LPR, physical chunk l%LPR and
-  // fetches the logical chunk the row's swizzle maps there.  The source is
-  // the head's base advanced to the super-tile (scalar) plus a per-lane
-  // offset that is the same for every super-tile; only a super-tile that
-  // crosses the cache end computes clamped offsets (rows past kv_len - 1
-  // re-read row kv_len - 1: finite data, and those keys are masked).
+  // fetches the logical chunk the row's swizzle maps there.  The source is a
+  // per-lane address fixed for the whole loop, advanced by the super-tile's
+  // (scalar) offset; only a super-tile that crosses the cache end computes
+  // clamped rows (rows past kv_len - 1 re-read row kv_len - 1: finite data,
+  // and those keys are masked).
   int crow[NCP];
   uint32_t kcb[NCP], vcb[NCP], kof[NCP], vof[NCP];
 #pragma unroll
@@ -630,23 +631,29 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(RPC * wave * ROWB));
   const char* kbase = reinterpret_cast<const char*>(kh_ptr);
   const char* vbase = reinterpret_cast<const char*>(vh_ptr);
+  const char* kl[NCP];
+  const char* vl[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    kl[i] = kbase + kof[i];
+    vl[i] = vbase + vof[i];
+  }
   auto issue = [&](char* st, int super) {
     const int kv0 = super * KS * BN;
     const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     if (kv0 + KS * BN <= kv_len) {
-      const char* kb = kbase + (int64_t)kv0 * ROWB;
-      const char* vb = vbase + (int64_t)kv0 * ROWB;
+      const int64_t off = (int64_t)kv0 * ROWB;
 #pragma unroll
       for (int i = 0; i < NCP; ++i) {
-        dma16(kb, kof[i], mk + i * (RPC * 4 * KS * ROWB));
-        dma16(vb, vof[i], mv + i * (RPC * 4 * KS * ROWB));
+        dma16(kl[i] + off, mk + i * (RPC * 4 * KS * ROWB));
+        dma16(vl[i] + off, mv + i * (RPC * 4 * KS * ROWB));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NCP; ++i) {
         const uint32_t rb = (uint32_t)min(kv0 + crow[i], kv_len - 1) * ROWB;
-        dma16(kbase, rb + kcb[i], mk + i * (RPC * 4 * KS * ROWB));
-        dma16(vbase, rb + vcb[i], mv + i * (RPC * 4 * KS * ROWB));
+        dma16(kbase + (rb + kcb[i]), mk + i * (RPC * 4 * KS * ROWB));
+        dma16(vbase + (rb + vcb[i]), mv + i * (RPC * 4 * KS * ROWB));
       }
     }
   };
