@@ -324,11 +324,12 @@ __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, 
 // update, O^T += V^T P^T on MFMA.  TWO: the tile's second 32-key block is
 // visible to some row of this wave (false only on causal diagonal tiles and
 // at the cache end).  MASK: some key of the tile is invisible to some row.
-// primed (wave-uniform): every row of the wave has a finite offset m.
-template <typename T, bool TWO, bool MASK, bool CAUSAL>
+// SPEC: take the probabilities at the current offset first (false for a
+// wave's first tile, whose offsets are not set yet: straight to the maximum).
+template <typename T, bool TWO, bool MASK, bool CAUSAL, bool SPEC = true>
 __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typename Half16<T>::vec8 (&qop)[4],
-                                       f32x16 (&acc)[2], float& m, float& l, bool& primed, const float cc,
-                                       const int kv0, const int kv_len, const int pos, const int lane) {
+                                       f32x16 (&acc)[2], float& m, float& l, const float cc, const int kv0,
+                                       const int kv_len, const int pos, const int lane) {
   typedef Half16<T> H;
   typedef typename H::vec8 vec8;
   constexpr int NB = TWO ? 2 : 1;
@@ -387,25 +388,27 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
         }
   }
 
-  // Steady state: take the probabilities at the current offset.  Before the
-  // offsets are set, or if any lane's block sum is out of range, go through
-  // the maximum.  One call site keeps a single rescale point for acc.
+  // Take the probabilities at the current offset.  If some lane's offset is
+  // not set yet (m = -inf: its row has seen no key) or its block sum is out
+  // of range, redo the tile through the maximum: re-read K (s is consumed by
+  // then, so no score register lives across the branch), raise the offset,
+  // recompute.  The test is per lane and comes after the probabilities, so
+  // the steady case is one straight-line block; one call site keeps a single
+  // rescale point for acc.
   u32x4 pw[NB][2];
-  float ts = 0.f;
-  bool need_max = !primed;
-  if (primed) {
+  float ts;
+  if constexpr (SPEC) {
     ts = probs16<T, NB>(s, cc, m, pw);
-    need_max = __any(ts > P_LIMIT);
-  }
-  if (need_max) {
-    // s is dead past this point either way: re-read K and recompute it here
-    // so no score register lives across the branch.
-    asm volatile("" ::: "memory");
-    f32x16 s2[NB];
-    scores(s2);
-    const float moff = online_offset<NB>(s2, acc, m, l, cc);  // may rescale acc and l
-    ts = probs16<T, NB>(s2, cc, moff, pw);
-    primed = __all(m != -INFINITY);
+    if (__any(ts > P_LIMIT || m == -INFINITY)) {
+      asm volatile("" ::: "memory");
+      f32x16 s2[NB];
+      scores(s2);
+      const float moff = online_offset<NB>(s2, acc, m, l, cc);  // may rescale acc and l
+      ts = probs16<T, NB>(s2, cc, moff, pw);
+    }
+  } else {
+    const float moff = online_offset<NB>(s, acc, m, l, cc);  // may rescale acc and l
+    ts = probs16<T, NB>(s, cc, moff, pw);
   }
   l += ts;
 
@@ -638,17 +641,22 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     kl[i] = kbase + kof[i];
     vl[i] = vbase + vof[i];
   }
+  // A super-tile entirely below the cache end.
+  auto issue_full = [&](char* st, int super) {
+    const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
+    const int64_t off = (int64_t)super * KS * BN * ROWB;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      dma16(kl[i] + off, mk + i * (RPC * 4 * KS * ROWB));
+      dma16(vl[i] + off, mv + i * (RPC * 4 * KS * ROWB));
+    }
+  };
   auto issue = [&](char* st, int super) {
     const int kv0 = super * KS * BN;
-    const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     if (kv0 + KS * BN <= kv_len) {
-      const int64_t off = (int64_t)kv0 * ROWB;
-#pragma unroll
-      for (int i = 0; i < NCP; ++i) {
-        dma16(kl[i] + off, mk + i * (RPC * 4 * KS * ROWB));
-        dma16(vl[i] + off, mv + i * (RPC * 4 * KS * ROWB));
-      }
+      issue_full(st, super);
     } else {
+      const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
 #pragma unroll
       for (int i = 0; i < NCP; ++i) {
         const uint32_t rb = (uint32_t)min(kv0 + crow[i], kv_len - 1) * ROWB;
@@ -666,7 +674,6 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   }
   float m = -INFINITY;  // exponent offset (log2 units), per row
   float l = 0.f;        // this lane's share of the row sum
-  bool primed = false;  // every row of this wave has a finite offset (wave-uniform)
   const float cc = p.c;
 
   auto compute = [&](const char* st, int super) {
@@ -697,35 +704,39 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     } else {
       if (blk1) {
         if (need_mask)
-          tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
+          tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
         else
-          tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
+          tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
       } else {
         if (need_mask)
-          tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
+          tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
         else
-          tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
+          tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
       }
     }
   };
 
   // Tiles every wave of the workgroup sees in full (all keys below the cache
   // end and, when causal, at or before the workgroup's first row): the
-  // leading super-steps made only of such tiles run a loop without any
-  // visibility or mask logic.
+  // leading super-steps made only of such tiles, whose prefetched super-tile
+  // also lies entirely below the cache end, run a loop without conditions:
+  // no visibility, mask or clamp logic, fixed waits, and every wave computes
+  // (one whose rows all lie past the window's end is never stored).
   int t_full = kv_len / BN;
   if (CAUSAL) t_full = min(t_full, (row0 + shift + 1) / BN);
-  const int j_full = t_full / KS;
-  auto compute_full = [&](const char* st, int super) {
-    if (!wave_live) return;
+  int j_full = min(t_full / KS, min(kv_len / (KS * BN), n_super) - (NS - 1));
+  j_full = j_full > 0 ? j_full - j_full % NS : 0;
+  auto compute_full = [&](const char* st, int super, auto spec) {
     const char* ks = st + kh * TILE;
     const char* vs = st + KS * TILE + kh * TILE;
     const int kv0 = (super * KS + kh) * BN;
     if constexpr (F32)
       tile32<true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
     else
-      tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, primed, cc, kv0, kv_len, pos, lane);
+      tile16<T, true, false, CAUSAL, decltype(spec)::value>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
   };
+  const std::true_type spec;       // offsets set: speculate
+  const std::false_type first;     // a wave's first tile
 
   int j = 0;
   if constexpr (NS == 3) {
@@ -742,13 +753,27 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     };
     if (n_super > 0) issue(st0, 0);
     if (n_super > 1) issue(st1, 1);
-    for (; j + 3 <= j_full; j += 3) {
-      sync(st2, j);
-      compute_full(st0, j);
-      sync(st0, j + 1);
-      compute_full(st1, j + 1);
-      sync(st1, j + 2);
-      compute_full(st2, j + 2);
+    auto sync_full = [&](char* nxt, int j) {
+      wait_vmem<2 * NCP>();
+      barrier_keep_dma();
+      issue_full(nxt, j + 2);
+    };
+    if (j_full > 0) {  // the first group: its first tile sets the offsets
+      sync_full(st2, 0);
+      compute_full(st0, 0, first);
+      sync_full(st0, 1);
+      compute_full(st1, 1, spec);
+      sync_full(st1, 2);
+      compute_full(st2, 2, spec);
+      j = 3;
+    }
+    for (; j < j_full; j += 3) {
+      sync_full(st2, j);
+      compute_full(st0, j, spec);
+      sync_full(st0, j + 1);
+      compute_full(st1, j + 1, spec);
+      sync_full(st1, j + 2);
+      compute_full(st2, j + 2, spec);
     }
     for (; j < n_super; j += 3) {
       sync(st2, j);
@@ -768,11 +793,23 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
       if (j + 1 < n_super) issue(nxt, j + 1);
     };
     if (n_super > 0) issue(st0, 0);
-    for (; j + 2 <= j_full; j += 2) {
-      sync(st1, j);
-      compute_full(st0, j);
-      sync(st0, j + 1);
-      compute_full(st1, j + 1);
+    auto sync_full = [&](char* nxt, int j) {
+      wait_vmem<0>();
+      barrier_keep_dma();
+      issue_full(nxt, j + 1);
+    };
+    if (j_full > 0) {  // the first pair: its first tile sets the offsets
+      sync_full(st1, 0);
+      compute_full(st0, 0, first);
+      sync_full(st0, 1);
+      compute_full(st1, 1, spec);
+      j = 2;
+    }
+    for (; j < j_full; j += 2) {
+      sync_full(st1, j);
+      compute_full(st0, j, spec);
+      sync_full(st0, j + 1);
+      compute_full(st1, j + 1, spec);
     }
     for (; j < n_super; j += 2) {
       sync(st1, j);
