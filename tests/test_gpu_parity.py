@@ -113,6 +113,30 @@ def test_many_tile_grids(dtype):
     check(q, k, v, dtype, True, chunk=100, kv_len=320, what="16x16 heads chunk 100 kv_len 320")
 
 
+MANY_TILES = [  # (B, H, S_q, S_kv, causal, chunk, kv_len, scale): > 512 query tiles
+    (32, 16, 200, 200, True, None, None, None),      # query tiles over 2 and 4 key tiles
+    (64, 8, 130, 70, False, None, None, None),       # 2 key tiles, the second clamped at the cache end
+    (64, 16, 130, 40, False, None, None, None),      # a single key tile (the staging stage is unused)
+    (16, 16, 600, 1000, True, 250, 900, None),       # windows over a partly filled cache
+    (7, 13, 700, 700, True, None, None, None),       # B*H not a multiple of 8: no XCD grouping
+    (32, 16, 200, 200, True, None, None, -0.125),    # negative scale
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_many_tile_shapes(dtype):
+    """16-bit grids with more than two query tiles per CU (one wave group per
+    tile, three LDS stages; the epilogue is staged in the stage of the
+    second-to-last key tile): one, two and four key tiles, a clamped cache-end tile, windows over a partly
+    filled cache, heads not grouped by XCD, and a negative scale."""
+    for n, (B, H, S_q, S_kv, causal, chunk, kv_len, scale) in enumerate(MANY_TILES):
+        w = W.Workload("many", B, H, S_q, S_kv, 64, causal, (dtype,), seed=120 + n)
+        q, k, v = W.make_inputs(w, dtype)
+        say(f"[parity] many tiles {(B, H, S_q, S_kv, causal, chunk, kv_len, scale)} {dtype}")
+        check(q, k, v, dtype, causal, scale=scale, chunk=chunk, kv_len=kv_len,
+              what=f"many tiles {(B, H, S_q, S_kv, causal, chunk, kv_len, scale)} {dtype}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_causal_offsets(dtype):
     """Bottom-right causal with S_kv - S_q in {1 .. 100}: some query rows see no

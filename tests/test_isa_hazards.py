@@ -10,7 +10,9 @@ operands are restricted to forms that need no wait states from it:
   v_readfirstlane, v_cmp) needs wait states the compiler cannot insert here;
 * the one wait state an SALU write of M0 needs before an LDS-DMA instruction
   reads it is part of the assembly: no LDS-DMA instruction may directly follow
-  an instruction whose destination is M0.
+  an instruction whose destination is M0;
+* M0 itself is written by scalar instructions only (a VALU write of an SGPR
+  read by a VMEM instruction would need wait states as above).
 """
 import os
 import subprocess
@@ -58,3 +60,21 @@ def test_lds_dma_addresses_come_from_vgprs(tmp_path):
     assert dma, "no LDS-DMA instruction found"
     sgpr_based = [ins for ins in dma if ins.split(None, 1)[1].split(",")[1].strip() != "off"]
     assert not sgpr_based, f"{len(sgpr_based)} LDS-DMA instructions take an SGPR base, e.g. {sgpr_based[0]}"
+
+
+def test_m0_for_lds_dma_written_by_scalar_instructions(tmp_path):
+    # A VMEM instruction reading an SGPR (M0 included) that a VALU instruction
+    # wrote needs wait states the assembly does not carry: M0 must come from
+    # SALU (s_mov/s_add ...), never v_readfirstlane/v_readlane.
+    asm = _device_asm(tmp_path)
+    last_m0, n, bad = None, 0, []
+    for ins in _instructions(asm):
+        if ins.split()[0].startswith("global_load_lds"):
+            n += 1
+            if last_m0 is None or not last_m0.startswith("s_"):
+                bad.append((last_m0, ins))
+        parts = ins.split(None, 1)
+        if len(parts) > 1 and parts[1].split(",")[0].strip() == "m0":
+            last_m0 = ins
+    assert n > 0, "no LDS-DMA instruction found"
+    assert not bad, f"{len(bad)} LDS-DMA instructions take M0 from a non-scalar write, e.g. {bad[0]}"

@@ -338,7 +338,7 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
   // S^T = K Q^T; k-step t: lane holds K[32kb + c][32hf + 8t .. +7].  Keys
   // this lane's row cannot see get -inf (exp2(-inf) = 0); only diagonal and
   // cache-end tiles carry the mask.
-  auto scores = [&](f32x16 (&s)[NB]) {
+  auto scores = [&](f32x16 (&s)[NB], const int k0) {
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -355,14 +355,14 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
           const bool vis = key < kv_len && (!CAUSAL || key <= pos);
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
   };
   f32x16 s[NB];
-  scores(s);
+  scores(s, kv0);
 
   // V^T operands, read transposed from the [key][d] tile before the softmax
   // so their latency overlaps it.  Operand (kb, u, dt), k-slot 8hf + e, holds
@@ -401,8 +401,12 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
     ts = probs16<T, NB>(s, cc, m, pw);
     if (__any(ts > P_LIMIT || m == -INFINITY)) {
       asm volatile("" ::: "memory");
+      // An opaque copy of kv0: the masks are recomputed here rather than the
+      // first pass's 32 lane masks being kept in scalar registers meanwhile.
+      int k0 = kv0;
+      asm volatile("" : "+v"(k0));
       f32x16 s2[NB];
-      scores(s2);
+      scores(s2, k0);
       const float moff = online_offset<NB>(s2, acc, m, l, cc);  // may rescale acc and l
       ts = probs16<T, NB>(s2, cc, moff, pw);
     }
@@ -860,42 +864,66 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     }
   }
 
-  // Epilogue: O = acc / l, rounded to T, for the rows this wave owns.
+  // Epilogue: O = acc / l, rounded to T, for the rows this wave owns.  The
+  // wave's 32-row tile is staged row-major in LDS (16-byte chunks XOR-swizzled
+  // by row) and stored as whole rows, 64 lanes x 16 bytes per store: a store
+  // of the accumulator layout directly would touch 32 rows per instruction
+  // with 8- or 16-byte pieces.  Staging space: with one wave group, the stage
+  // of the second-to-last key tile (every wave has passed it and no copy
+  // targets it any more); with the key split, the wave's own part of the
+  // merge area, which it has read.
   const float lt = l + other_half(l);
   const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
-  if (qrow < row1) {
-    T* orow = oh + (int64_t)qrow * HEAD_DIM;
-    if constexpr (F32) {
-      // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
-      // 4g .. 4g+3 of both accumulators cover columns 16g + 8hf .. +7.
+  char* ot;
+  if constexpr (KS == 1) {
+    const int os = (n_super + 1) % 3;
+    ot = (os == 0 ? st0 : os == 1 ? st1 : st2) + wave * (32 * ROWB);
+  } else {
+    ot = st0 + qg * (8 * 64 * 16);
+  }
+  if constexpr (F32) {
+    // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
+    // 4g .. 4g+3 of both accumulators cover columns 16g + 8hf .. +7.
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int ch = 4 * gq + 2 * hf;  // 16-byte chunk of columns 16g + 8hf .. +3
+      u32x4 w0, w1;
+      w0[0] = __float_as_uint(acc[0][4 * gq] * inv);
+      w0[1] = __float_as_uint(acc[1][4 * gq] * inv);
+      w0[2] = __float_as_uint(acc[0][4 * gq + 1] * inv);
+      w0[3] = __float_as_uint(acc[1][4 * gq + 1] * inv);
+      w1[0] = __float_as_uint(acc[0][4 * gq + 2] * inv);
+      w1[1] = __float_as_uint(acc[1][4 * gq + 2] * inv);
+      w1[2] = __float_as_uint(acc[0][4 * gq + 3] * inv);
+      w1[3] = __float_as_uint(acc[1][4 * gq + 3] * inv);
+      *reinterpret_cast<u32x4*>(ot + c * 256 + 16 * (ch ^ (c & 15))) = w0;
+      *reinterpret_cast<u32x4*>(ot + c * 256 + 16 * ((ch + 1) ^ (c & 15))) = w1;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // rows 4k .. 4k+3
+      const int row = 4 * k + lane / 16, ch = lane % 16;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 256 + 16 * (ch ^ (row & 15)));
+      if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 4 * ch) = x;
+    }
+  } else {
+    typedef Half16<T> H;
+    // acc[dt] register r is column 32dt + 8(r/4) + 4hf + r%4: registers 4g ..
+    // 4g+3 are the half-chunk 8hf of 16-byte chunk 4dt + g.
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int d = 16 * gq + 8 * hf;
-        u32x4 w0, w1;
-        w0[0] = __float_as_uint(acc[0][4 * gq] * inv);
-        w0[1] = __float_as_uint(acc[1][4 * gq] * inv);
-        w0[2] = __float_as_uint(acc[0][4 * gq + 1] * inv);
-        w0[3] = __float_as_uint(acc[1][4 * gq + 1] * inv);
-        w1[0] = __float_as_uint(acc[0][4 * gq + 2] * inv);
-        w1[1] = __float_as_uint(acc[1][4 * gq + 2] * inv);
-        w1[2] = __float_as_uint(acc[0][4 * gq + 3] * inv);
-        w1[3] = __float_as_uint(acc[1][4 * gq + 3] * inv);
-        *reinterpret_cast<u32x4*>(orow + d) = w0;
-        *reinterpret_cast<u32x4*>(orow + d + 4) = w1;
+        u32x2 w;
+        w[0] = H::pack2(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv);
+        w[1] = H::pack2(acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x2*>(ot + c * 128 + 16 * ((4 * dt + gq) ^ (c & 7)) + 8 * hf) = w;
       }
-    } else {
-      typedef Half16<T> H;
+    }
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int d = 32 * dt + 8 * gq + 4 * hf;
-          u32x2 w;
-          w[0] = H::pack2(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv);
-          w[1] = H::pack2(acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
-        }
-      }
+    for (int k = 0; k < 4; ++k) {  // rows 8k .. 8k+7
+      const int row = 8 * k + lane / 8, ch = lane % 8;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 128 + 16 * (ch ^ (row & 7)));
+      if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 8 * ch) = x;
     }
   }
 }
