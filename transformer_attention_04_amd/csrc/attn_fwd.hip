@@ -594,22 +594,6 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   // Q operand (B operand of S^T = K Q^T), resident for the whole key loop.
   // 16-bit: k-step t holds Q[qrow][32hf + 8t .. +7]; fp32: k-step t holds Q[qrow][32hf + t].
   typename std::conditional<F32, float[32], typename Half16<typename std::conditional<F32, __bf16, T>::type>::vec8[4]>::type qop;
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * HEAD_DIM + 32 * hf);
-    constexpr int NQ = F32 ? 8 : 4;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < row1) x = src[j];
-      x ^= p.q_flip;
-      if constexpr (F32) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qop[4 * j + e] = __uint_as_float(x[e]);
-      } else {
-        qop[j] = __builtin_bit_cast(typename std::remove_reference<decltype(qop[0])>::type, x);
-      }
-    }
-  }
 
   // Tile copies: copy i of wave w fills stage rows RPC*(4*KS*i + w) .. +RPC-1
   // of K and of V; lane l lands in row + l/LPR, physical chunk l%LPR and
@@ -666,6 +650,47 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
         const uint32_t rb = (uint32_t)min(kv0 + crow[i], kv_len - 1) * ROWB;
         dma16(kbase + (rb + kcb[i]), mk + i * (RPC * 4 * KS * ROWB));
         dma16(vbase + (rb + vcb[i]), mv + i * (RPC * 4 * KS * ROWB));
+      }
+    }
+  };
+
+  // Each wave copies its own 32 Q rows (whole rows, K's swizzle) into its own
+  // slab of the stage that the first step refills, ahead of the first K/V
+  // copies, and reads them into the MFMA operand after its first wait --
+  // its own copies only, so no barrier is needed before the read -- and
+  // before that step's barrier.  Whole-row copies instead of per-lane loads
+  // that touch 32 rows each, and the first step waits only for what it needs.
+  // Rows past the tile's end re-read its last row (never stored).
+  constexpr int SLAB = 32 * ROWB;  // one wave's Q rows; 4 KS slabs fit in a stage
+  char* const qst = NS == 3 ? st2 : st1;
+  const uint32_t wslab = __builtin_amdgcn_readfirstlane((uint32_t)(wave * SLAB));
+  {
+    const uint32_t mq = lds_addr(qst) + wslab;
+    const char* qb = reinterpret_cast<const char*>(qh);
+#pragma unroll
+    for (int i = 0; i < SLAB / 1024; ++i) {
+      const int row = RPC * i + lane / LPR;  // row of the slab
+      const int ph = lane % LPR;
+      const uint32_t cb = F32 ? 16 * (ph ^ (row & 15)) : 16 * (ph ^ ((row & 7) ^ ((row >> 3) & 1)));
+      dma16(qb + ((int64_t)min(wrow0 + row, row1 - 1) * ROWB + cb), mq + i * 1024);
+    }
+  }
+  auto read_q = [&]() {
+    const char* qs = qst + wslab;
+    if constexpr (F32) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qs + k32_off(c, 8 * hf + j));
+        x ^= p.q_flip;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qop[4 * j + e] = __uint_as_float(x[e]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qs + k16_off(c, 4 * hf + t));
+        x ^= p.q_flip;
+        qop[t] = __builtin_bit_cast(typename std::remove_reference<decltype(qop[0])>::type, x);
       }
     }
   };
@@ -757,6 +782,12 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     };
     if (n_super > 0) issue(st0, 0);
     if (n_super > 1) issue(st1, 1);
+    // The Q rows and super-tile 0 (copied before super-tile 1).
+    if (n_super > 1)
+      wait_vmem<2 * NCP>();
+    else
+      wait_vmem<0>();
+    read_q();
     auto sync_full = [&](char* nxt, int j) {
       wait_vmem<2 * NCP>();
       barrier_keep_dma();
@@ -797,6 +828,8 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
       if (j + 1 < n_super) issue(nxt, j + 1);
     };
     if (n_super > 0) issue(st0, 0);
+    wait_vmem<0>();  // the Q rows (and super-tile 0)
+    read_q();
     auto sync_full = [&](char* nxt, int j) {
       wait_vmem<0>();
       barrier_keep_dma();
@@ -874,6 +907,10 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   // merge area, which it has read.
   const float lt = l + other_half(l);
   const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
+  // An opaque lane index: the store rows below equal the Q copy rows of the
+  // prologue, which the compiler would otherwise keep live across the loop.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
   char* ot;
   if constexpr (KS == 1) {
     const int os = (n_super + 1) % 3;
@@ -901,7 +938,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {  // rows 4k .. 4k+3
-      const int row = 4 * k + lane / 16, ch = lane % 16;
+      const int row = 4 * k + ln / 16, ch = ln % 16;
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 256 + 16 * (ch ^ (row & 15)));
       if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 4 * ch) = x;
     }
@@ -921,7 +958,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // rows 8k .. 8k+7
-      const int row = 8 * k + lane / 8, ch = lane % 8;
+      const int row = 8 * k + ln / 8, ch = ln % 8;
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 128 + 16 * (ch ^ (row & 7)));
       if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 8 * ch) = x;
     }
