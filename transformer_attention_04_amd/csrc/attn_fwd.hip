@@ -162,6 +162,11 @@ __device__ __forceinline__ float max_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// True if the predicate holds on some active lane: the ballot's lane mask is
+// tested directly (__any converts the predicate to an integer first, two
+// extra vector instructions).
+__device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
 // from this lane's 64-bit address gsrc (a VGPR pair); lane l's bytes land at
 // LDS address m0 + 16*l, m0 wave-uniform.  Issued as inline assembly so the
@@ -227,7 +232,7 @@ __device__ __forceinline__ float online_offset(const f32x16 (&s)[NB], f32x16 (&a
   x = max_halves(x);
   const float xc = (x == -INFINITY) ? -INFINITY : x * cc;
   const bool raise = xc > m + LAZY_TH;
-  if (__any(raise)) {
+  if (any_lane(raise)) {
     // Raising lanes scale by exp2(m - xc) (0 when m was -inf); the others keep
     // their offset and scale by exactly 1 (m may still be -inf there: rows
     // that have not seen a visible key yet, so m - m would be NaN).
@@ -326,7 +331,9 @@ __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, 
 // at the cache end).  MASK: some key of the tile is invisible to some row.
 // SPEC: take the probabilities at the current offset first (false for a
 // wave's first tile, whose offsets are not set yet: straight to the maximum).
-template <typename T, bool TWO, bool MASK, bool CAUSAL, bool SPEC = true>
+// MSET: every lane's offset is known to be set (after a first tile that every
+// row of the wave sees in full), so only the block sums are checked.
+template <typename T, bool TWO, bool MASK, bool CAUSAL, bool SPEC = true, bool MSET = false>
 __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typename Half16<T>::vec8 (&qop)[4],
                                        f32x16 (&acc)[2], float& m, float& l, const float cc, const int kv0,
                                        const int kv_len, const int pos, const int lane) {
@@ -399,7 +406,7 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
   float ts;
   if constexpr (SPEC) {
     ts = probs16<T, NB>(s, cc, m, pw);
-    if (__any(ts > P_LIMIT || m == -INFINITY)) {
+    if (any_lane(ts > P_LIMIT || (!MSET && m == -INFINITY))) {
       asm volatile("" ::: "memory");
       // An opaque copy of kv0: the masks are recomputed here rather than the
       // first pass's 32 lane masks being kept in scalar registers meanwhile.
@@ -750,7 +757,9 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   // leading super-steps made only of such tiles, whose prefetched super-tile
   // also lies entirely below the cache end, run a loop without conditions:
   // no visibility, mask or clamp logic, fixed waits, and every wave computes
-  // (one whose rows all lie past the window's end is never stored).
+  // (one whose rows all lie past the window's end is never stored).  The
+  // first such tile is taken with the row maximum and gives every lane an
+  // offset, so the later ones check only their block sums.
   int t_full = kv_len / BN;
   if (CAUSAL) t_full = min(t_full, (row0 + shift + 1) / BN);
   int j_full = min(t_full / KS, min(kv_len / (KS * BN), n_super) - (NS - 1));
@@ -762,9 +771,10 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     if constexpr (F32)
       tile32<true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
     else
-      tile16<T, true, false, CAUSAL, decltype(spec)::value>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+      tile16<T, true, false, CAUSAL, decltype(spec)::value, decltype(spec)::value>(ks, vs, qop, acc, m, l, cc, kv0,
+                                                                                  kv_len, pos, lane);
   };
-  const std::true_type spec;       // offsets set: speculate
+  const std::true_type spec;       // offsets set (every lane): speculate
   const std::false_type first;     // a wave's first tile
 
   int j = 0;
