@@ -5,8 +5,8 @@ The K/V tile copies are `global_load_lds_dwordx4` instructions written as inline
 assembly, which the compiler's hazard recognizer does not look into, so their
 operands are restricted to forms that need no wait states from it:
 
-* the global address comes from a VGPR pair (`..., off`), never from an SGPR
-  base: a VMEM read of an SGPR written by a VALU instruction (v_readlane,
+* the global address comes from a VGPR pair (`..., off` with an optional
+  immediate offset), never from an SGPR base: a VMEM read of an SGPR written by a VALU instruction (v_readlane,
   v_readfirstlane, v_cmp) needs wait states the compiler cannot insert here;
 * the one wait state an SALU write of M0 needs before an LDS-DMA instruction
   reads it is part of the assembly: no LDS-DMA instruction may directly follow
@@ -58,7 +58,7 @@ def test_lds_dma_addresses_come_from_vgprs(tmp_path):
     asm = _device_asm(tmp_path)
     dma = [ins for ins in _instructions(asm) if ins.split()[0].startswith("global_load_lds")]
     assert dma, "no LDS-DMA instruction found"
-    sgpr_based = [ins for ins in dma if ins.split(None, 1)[1].split(",")[1].strip() != "off"]
+    sgpr_based = [ins for ins in dma if ins.split(None, 1)[1].split(",")[1].split()[0] != "off"]
     assert not sgpr_based, f"{len(sgpr_based)} LDS-DMA instructions take an SGPR base, e.g. {sgpr_based[0]}"
 
 

@@ -182,6 +182,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
 
+// Two copies whose sources and destinations both lie 4096 bytes apart, from
+// one address and one M0 at their midpoint: the instruction offset (13-bit
+// signed) applies to the global and the LDS address alike, so the copies
+// take offsets -2048 and +2048.  Same operand rules as dma16.
+__device__ __forceinline__ void dma16_pair(const void* gmid, uint32_t m0mid) {
+  asm volatile(
+      "s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:-2048\n\tglobal_load_lds_dwordx4 %0, off offset:2048" ::"v"(gmid),
+      "{m0}"(m0mid)
+      : "memory");
+}
+
 // LDS byte address of a __shared__ location (what M0 takes).
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
@@ -308,7 +319,7 @@ template <typename T, int NB>
 __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, const float moff,
                                          u32x4 (&pw)[NB][2]) {
   typedef Half16<T> H;
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
+  float ls[2] = {0.f, 0.f};  // independent partial sums
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -320,9 +331,9 @@ __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, 
         const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
         const unsigned w = H::pack2(e0, e1);
         pw[kb][u][q] = w;
-        ls[q] = H::add_pair(w, ls[q]);
+        ls[q & 1] = H::add_pair(w, ls[q & 1]);
       }
-  return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  return ls[0] + ls[1];
 }
 
 // One wave's work on one 64-key tile: S^T = K Q^T on MFMA, online-softmax
@@ -637,13 +648,25 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     vl[i] = vbase + vof[i];
   }
   // A super-tile entirely below the cache end.
+  // Copy i + 1 lies CSTEP bytes after copy i in the source (its rows are
+  // CSTEP / ROWB further on, with the same swizzle) and in the stage; at 4096
+  // bytes (one wave group) consecutive copies go in pairs (dma16_pair).
+  constexpr int CSTEP = RPC * 4 * KS * ROWB;
   auto issue_full = [&](char* st, int super) {
     const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     const int64_t off = (int64_t)super * KS * BN * ROWB;
+    if constexpr (CSTEP == 4096 && NCP % 2 == 0) {
 #pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      dma16(kl[i] + off, mk + i * (RPC * 4 * KS * ROWB));
-      dma16(vl[i] + off, mv + i * (RPC * 4 * KS * ROWB));
+      for (int i = 0; i < NCP; i += 2) {
+        dma16_pair(kl[i] + (off + 2048), mk + i * CSTEP + 2048);
+        dma16_pair(vl[i] + (off + 2048), mv + i * CSTEP + 2048);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        dma16(kl[i] + off, mk + i * CSTEP);
+        dma16(vl[i] + off, mv + i * CSTEP);
+      }
     }
   };
   auto issue = [&](char* st, int super) {
@@ -655,8 +678,8 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
 #pragma unroll
       for (int i = 0; i < NCP; ++i) {
         const uint32_t rb = (uint32_t)min(kv0 + crow[i], kv_len - 1) * ROWB;
-        dma16(kbase + (rb + kcb[i]), mk + i * (RPC * 4 * KS * ROWB));
-        dma16(vbase + (rb + vcb[i]), mv + i * (RPC * 4 * KS * ROWB));
+        dma16(kbase + (rb + kcb[i]), mk + i * CSTEP);
+        dma16(vbase + (rb + vcb[i]), mv + i * CSTEP);
       }
     }
   };
