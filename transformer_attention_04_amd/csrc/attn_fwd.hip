@@ -613,18 +613,21 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   // 16-bit: k-step t holds Q[qrow][32hf + 8t .. +7]; fp32: k-step t holds Q[qrow][32hf + t].
   typename std::conditional<F32, float[32], typename Half16<typename std::conditional<F32, __bf16, T>::type>::vec8[4]>::type qop;
 
-  // Tile copies: copy i of wave w fills stage rows RPC*(4*KS*i + w) .. +RPC-1
-  // of K and of V; lane l lands in row + l/LPR, physical chunk l%LPR and
-  // fetches the logical chunk the row's swizzle maps there.  The source is a
-  // per-lane address fixed for the whole loop, advanced by the super-tile's
-  // (scalar) offset; only a super-tile that crosses the cache end computes
-  // clamped rows (rows past kv_len - 1 re-read row kv_len - 1: finite data,
-  // and those keys are masked).
+  // Tile copies: the waves of key half kh copy its 64-row tile of K and of V;
+  // copy i of wave (kh, qg) fills stage rows 64 kh + RPC*(4i + qg) .. +RPC-1,
+  // lane l lands in row + l/LPR, physical chunk l%LPR and fetches the logical
+  // chunk the row's swizzle maps there.  The swizzle depends only on the low
+  // bits of the row, equal for all copies of a wave, so copy i + 1 lies
+  // 4 RPC rows = 4096 bytes after copy i in the source and in the stage.  The
+  // source is a per-lane address fixed for the whole loop, advanced by the
+  // super-tile's (scalar) offset; only a super-tile that crosses the cache
+  // end computes clamped rows (rows past kv_len - 1 re-read row kv_len - 1:
+  // finite data, and those keys are masked).
   int crow[NCP];
   uint32_t kcb[NCP], vcb[NCP], kof[NCP], vof[NCP];
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
-    const int row = RPC * (4 * KS * i + wave) + lane / LPR;
+    const int row = 64 * kh + RPC * (4 * i + qg) + lane / LPR;
     const int ph = lane % LPR;
     crow[i] = row;
     if constexpr (F32) {
@@ -637,7 +640,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     kof[i] = (uint32_t)row * ROWB + kcb[i];
     vof[i] = (uint32_t)row * ROWB + vcb[i];
   }
-  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(RPC * wave * ROWB));
+  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)((64 * kh + RPC * qg) * ROWB));
   const char* kbase = reinterpret_cast<const char*>(kh_ptr);
   const char* vbase = reinterpret_cast<const char*>(vh_ptr);
   const char* kl[NCP];
@@ -648,25 +651,17 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     vl[i] = vbase + vof[i];
   }
   // A super-tile entirely below the cache end.
-  // Copy i + 1 lies CSTEP bytes after copy i in the source (its rows are
-  // CSTEP / ROWB further on, with the same swizzle) and in the stage; at 4096
-  // bytes (one wave group) consecutive copies go in pairs (dma16_pair).
-  constexpr int CSTEP = RPC * 4 * KS * ROWB;
+  // Copy i + 1 lies CSTEP = 4096 bytes after copy i in the source and in the
+  // stage: consecutive copies go in pairs (dma16_pair).
+  constexpr int CSTEP = RPC * 4 * ROWB;
+  static_assert(CSTEP == 4096 && NCP % 2 == 0, "paired tile copies");
   auto issue_full = [&](char* st, int super) {
     const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     const int64_t off = (int64_t)super * KS * BN * ROWB;
-    if constexpr (CSTEP == 4096 && NCP % 2 == 0) {
 #pragma unroll
-      for (int i = 0; i < NCP; i += 2) {
-        dma16_pair(kl[i] + (off + 2048), mk + i * CSTEP + 2048);
-        dma16_pair(vl[i] + (off + 2048), mv + i * CSTEP + 2048);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NCP; ++i) {
-        dma16(kl[i] + off, mk + i * CSTEP);
-        dma16(vl[i] + off, mv + i * CSTEP);
-      }
+    for (int i = 0; i < NCP; i += 2) {
+      dma16_pair(kl[i] + (off + 2048), mk + i * CSTEP + 2048);
+      dma16_pair(vl[i] + (off + 2048), mv + i * CSTEP + 2048);
     }
   };
   auto issue = [&](char* st, int super) {
