@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a captured HIP graph")
+    ap.add_argument("--stream", action="store_true",
+                    help="chunked workloads: one step runs every query window in order, appending the "
+                         "window's K/V rows to a cache (attn_kv_append) and attending its queries to the "
+                         "grown cache (attn_fwd_chunked)")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-mb", type=float, default=None,
@@ -188,8 +192,27 @@ def main():
                 q, k, v = q0.clone(), k0.clone(), v0.clone()
             sets.append((q, k, v, torch.empty_like(q)))
     chunk = w.chunk
+    if args.stream:
+        if not chunk:
+            print("--stream needs a chunked workload", file=sys.stderr)
+            sys.exit(2)
+        # The window's new K/V rows and queries arrive as separate buffers;
+        # the cache holds NaN past kv_len (never read).
+        q, k, v, o = sets[0]
+        bounds = [(s, min(w.S_q, s + chunk)) for s in range(0, w.S_q, chunk)]
+        win = [tuple(x[:, :, a:b].contiguous() for x in (q, k, v, o)) for a, b in bounds]
+        kc = torch.full_like(k, float("nan"))
+        vc = torch.full_like(v, float("nan"))
+        del sets[:], q, k, v, o
+        log(f"[bench] streaming: {len(bounds)} windows of {chunk} rows")
 
     def step(i):
+        if args.stream:
+            kv = 0
+            for qw, kw, vw, ow in win:
+                kv = A.attn_kv_append(kc, vc, kw, vw, kv)
+                A.attn_fwd_chunked(qw, kc, vc, chunk=chunk, kv_len=kv, causal=w.causal, scale=w.scale, out=ow)
+            return
         q, k, v, o = sets[i % len(sets)]
         if chunk:
             A.attn_fwd_chunked(q, k, v, chunk=chunk, causal=w.causal, scale=w.scale, out=o)
@@ -235,11 +258,12 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_q": w.S_q, "S_kv": w.S_kv, "D_h": w.D,
-                   "causal": w.causal, "chunk": w.chunk, "rotating_sets": len(sets),
+                   "causal": w.causal, "chunk": w.chunk, "rotating_sets": 1 if args.stream else len(sets),
+                   "mode": "stream: append + attend per window" if args.stream else "single call",
                    "launch": "eager" if graph is None else "hip_graph_replay"},
         "roofline": roofline_for(w, dtype, sec),
     }
-    line["roofline"]["traffic"] = measured_traffic(w.name, dtype)
+    line["roofline"]["traffic"] = None if args.stream else measured_traffic(w.name, dtype)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)

@@ -124,6 +124,30 @@ int attn_fwd_chunked(const void *q, const void *k, const void *v, void *o,
                      int chunk, int kv_len);
 
 /*
+ * attn_kv_append -- write n_new new key and value rows into a K/V cache at
+ * row kv_len of every (b, h): the append step of a stream of bounded query
+ * windows against a growing key/value cache (page "Roofline", section "How
+ * we built it").  A streaming caller appends a window's K/V rows, then calls
+ * attn_fwd_chunked with S_q = that window's query rows and the grown kv_len
+ * (kv_len + n_new).
+ *   k_cache, v_cache : device [B, H, S_cap, D_h]; rows [kv_len, kv_len + n_new)
+ *                      of every head are overwritten, all other rows are left
+ *                      untouched.
+ *   k_new, v_new     : device [B, H, n_new, D_h], copied bit for bit.
+ *   kv_len           : rows already valid, 0 <= kv_len, kv_len + n_new <= S_cap.
+ *   D_h must be 64; dtype (enum attn_dtype) is the element type of all four.
+ * Same conventions as above: 16-byte aligned base pointers, asynchronous on
+ * `stream`, nothing allocated.  Errors: ATTN_E_NULL; ATTN_E_SHAPE (B, H,
+ * S_cap or n_new < 1, kv_len < 0, kv_len + n_new > S_cap, D_h != 64, sizes
+ * overflow); ATTN_E_DTYPE; ATTN_E_ALIGN; ATTN_E_OVERLAP (the two caches
+ * overlap, or a new-rows buffer overlaps a cache); ATTN_E_DEVICE;
+ * ATTN_E_LAUNCH.
+ */
+int attn_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                   int B, int H, int S_cap, int kv_len, int n_new, int D_h,
+                   int dtype, void *stream);
+
+/*
  * Schedule introspection (host only, no GPU needed).  attn_sched_grid writes the
  * number of workgroups one attn_fwd_chunked call with these sizes launches
  * (attn_fwd: chunk = S_q, kv_len = S_kv; causal as in the call, 0/1);

@@ -10,10 +10,14 @@ the explicit definition of Eq. A on the page "Shape-Aware Attention" (section
 causal rule "key j visible to query i iff j <= kv_len - S_q + i".  This module
 only marshals numpy arrays into it.
 
+``kv_append`` is the K/V cache append of the streaming use, a numpy slice
+assignment (no arithmetic).
+
 Parity status of each function is stated where it is tested (``tests/
 test_oracle_pins.py``): the attention function is pinned by closed forms,
 invariants, a library special case (torch CPU float64 SDPA with an explicit
-mask) and 50-digit brute force; it is not "parity unpinned".
+mask) and 50-digit brute force; ``kv_append`` by an element-by-element loop,
+two appends against one, and raw bit patterns; neither is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -109,3 +113,19 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
     if rc != 0:
         raise ValueError(f"oracle_attn_f64: {ORACLE_ERRORS.get(rc, rc)}")
     return o
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, kv_len):
+    """The K/V cache append of a stream of query windows against a growing
+    key/value cache (page "Roofline", section "How we built it"): copies of
+    the caches [B, H, S_cap, D] whose rows [kv_len, kv_len + n) of every
+    (b, h) are the new rows [B, H, n, D]; every other row is unchanged.  The
+    plain definition, a slice assignment on numpy arrays of any dtype (bit
+    patterns are copied as they are)."""
+    k_out, v_out = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    n = k_new.shape[2]
+    if kv_len < 0 or kv_len + n > k_out.shape[2]:
+        raise ValueError("kv_len + n exceeds the cache capacity")
+    k_out[:, :, kv_len:kv_len + n] = k_new
+    v_out[:, :, kv_len:kv_len + n] = v_new
+    return k_out, v_out

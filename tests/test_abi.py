@@ -162,3 +162,35 @@ def test_long_context_grid_size():
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(ImportError):
         A._load(str(tmp_path / "nope.so"))
+
+
+# attn_kv_append: fake caches of B=2, H=3, S_cap=100 rows, 5 new rows at kv_len 90.
+KC, VC, KN, VN = 0x1000000, 0x2000000, 0x3000000, 0x3100000
+GOOD_APPEND = dict(kc=KC, vc=VC, kn=KN, vn=VN, B=2, H=3, S_cap=100, kv_len=90, n=5, D=64, dtype=2)
+
+
+def call_append(**kw):
+    a = dict(GOOD_APPEND, **kw)
+    return A.lib.attn_kv_append(a["kc"], a["vc"], a["kn"], a["vn"], a["B"], a["H"], a["S_cap"], a["kv_len"],
+                                a["n"], a["D"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=0), 1), (dict(vc=0), 1), (dict(kn=0), 1), (dict(vn=0), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(S_cap=0), 2), (dict(n=0), 2), (dict(kv_len=-1), 2), (dict(D=128), 2),
+    (dict(kv_len=96), 2), (dict(kv_len=0, n=101), 2),   # past the cache capacity
+    (dict(B=1 << 16, H=1 << 15, S_cap=1 << 30, kv_len=0, n=1), 2),  # byte count overflow
+    (dict(dtype=5), 3),
+    (dict(kc=KC + 8), 7), (dict(vn=VN + 4), 7),
+    (dict(vc=KC + 4096), 8), (dict(kn=VC + 64), 8), (dict(vn=KC), 8),
+])
+def test_append_invalid_arguments_return_their_code(kw, code):
+    assert call_append(**kw) == code
+
+
+def test_append_valid_call_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_append() == 9
+    assert call_append(kv_len=0, n=100, dtype=0) == 9   # fills the whole cache

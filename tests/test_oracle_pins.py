@@ -97,3 +97,49 @@ def test_thread_count_does_not_change_results():
     a = oracle.attention(q, k, v, causal=True, threads=1)
     b = oracle.attention(q, k, v, causal=True, threads=4)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# the K/V cache append (a copy: pinned by brute force and its invariants)
+# ---------------------------------------------------------------------------
+def test_kv_append_brute_force():
+    rng = np.random.default_rng(3)
+    B, H, S, D, kv, n = 2, 3, 11, 5, 4, 6
+    kc, vc = rng.standard_normal((2, B, H, S, D)).astype(np.float32)
+    kn, vn = rng.standard_normal((2, B, H, n, D)).astype(np.float32)
+    kc0, vc0 = kc.copy(), vc.copy()
+    ko, vo = oracle.kv_append(kc, vc, kn, vn, kv)
+    for b in range(B):
+        for h in range(H):
+            for r in range(S):
+                for d in range(D):
+                    new = kv <= r < kv + n
+                    assert ko[b, h, r, d] == (kn[b, h, r - kv, d] if new else kc[b, h, r, d])
+                    assert vo[b, h, r, d] == (vn[b, h, r - kv, d] if new else vc[b, h, r, d])
+    assert np.array_equal(kc, kc0) and np.array_equal(vc, vc0)  # inputs untouched
+
+
+def test_kv_append_two_steps_equal_one():
+    rng = np.random.default_rng(4)
+    kc, vc = rng.standard_normal((2, 1, 2, 20, 3))
+    kn, vn = rng.standard_normal((2, 1, 2, 9, 3))
+    one = oracle.kv_append(kc, vc, kn, vn, 5)
+    a = oracle.kv_append(kc, vc, kn[:, :, :4], vn[:, :, :4], 5)
+    two = oracle.kv_append(a[0], a[1], kn[:, :, 4:], vn[:, :, 4:], 9)
+    assert np.array_equal(one[0], two[0]) and np.array_equal(one[1], two[1])
+
+
+def test_kv_append_copies_bit_patterns():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 1 << 16, size=(2, 1, 1, 8, 64), dtype=np.uint16)
+    bits[0, 0, 0, 0, :4] = [0x7FC1, 0xFF80, 0x7F80, 0x0001]  # NaN payload, -inf, +inf, a denormal (bf16)
+    new = rng.integers(0, 1 << 16, size=(2, 1, 1, 3, 64), dtype=np.uint16)
+    ko, vo = oracle.kv_append(bits[0], bits[1], new[0], new[1], 5)
+    assert np.array_equal(ko[:, :, 5:8], new[0]) and np.array_equal(ko[:, :, :5], bits[0][:, :, :5])
+    assert np.array_equal(vo[:, :, 5:8], new[1]) and np.array_equal(vo[:, :, :5], bits[1][:, :, :5])
+
+
+def test_kv_append_rejects_overflowing_capacity():
+    z = np.zeros((1, 1, 4, 2))
+    with pytest.raises(ValueError):
+        oracle.kv_append(z, z, np.zeros((1, 1, 3, 2)), np.zeros((1, 1, 3, 2)), 2)

@@ -7,6 +7,7 @@ built, importing this package raises.
 
     attn_fwd(q, k, v, causal=False, scale=None)            -> o
     attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o
+    attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len)   -> kv_len + n
     attn_strerror(status)                                    -> str
 
 q: [B, H, S_q, 64]; k, v: [B, H, S_kv, 64]; all contiguous, same dtype
@@ -28,7 +29,7 @@ STATUS = {
     5: "ATTN_E_CAUSAL", 6: "ATTN_E_CHUNK", 7: "ATTN_E_ALIGN", 8: "ATTN_E_OVERLAP",
     9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
+EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_kv_append", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
 
 
 class AttnError(RuntimeError):
@@ -47,6 +48,8 @@ def _load(path: str = LIB_PATH):
     lib.attn_fwd.restype = i
     lib.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, i, i]
     lib.attn_fwd_chunked.restype = i
+    lib.attn_kv_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.attn_kv_append.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_sched_grid.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i)]
@@ -147,6 +150,34 @@ def attn_fwd_chunked(q, k, v, chunk: int, kv_len: int | None = None, causal: boo
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o
+
+
+def attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len: int, stream=None) -> int:
+    """Write k_new, v_new [B, H, n, D] into rows [kv_len, kv_len + n) of the
+    caches [B, H, S_cap, D] (see attn_kv_append in include/attn.h); returns the
+    grown kv_len."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, D], got {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("caches and new rows must share a dtype")
+    if not (k_cache.device == v_cache.device == k_new.device == v_new.device):
+        raise ValueError("caches and new rows must be on one device")
+    B, H, S_cap, D = k_cache.shape
+    n = k_new.shape[2]
+    if v_cache.shape != k_cache.shape or k_new.shape != (B, H, n, D) or v_new.shape != k_new.shape:
+        raise ValueError(f"shape mismatch k_cache{tuple(k_cache.shape)} v_cache{tuple(v_cache.shape)} "
+                         f"k_new{tuple(k_new.shape)} v_new{tuple(v_new.shape)}")
+    dev = k_cache.device
+    st = _call(lib.attn_kv_append, dev, k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+               B, H, S_cap, int(kv_len), n, D, _dtype_code(k_cache), _stream_ptr(dev, stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return int(kv_len) + n
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, stream=None):

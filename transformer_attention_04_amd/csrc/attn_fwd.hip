@@ -1107,7 +1107,67 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+// ---------------------------------------------------------------------------
+// K/V cache append (streaming use of the chunked entry point)
+// ---------------------------------------------------------------------------
+// Head g's n_new new rows are one contiguous segment of the source, and land
+// contiguously at row kv_len of that head's cache: a plain copy, 16 bytes per
+// lane per step, K and V in the same launch.  blockIdx.x walks the segment in
+// blocks of APPEND_UNITS 16-byte units, blockIdx.y (and the loop) the heads.
+constexpr int APPEND_THREADS = 256;
+constexpr int APPEND_UNITS = APPEND_THREADS * 4;  // 16-byte units per block and head
+
+__global__ void __launch_bounds__(APPEND_THREADS) kv_append_kernel(char* kc, char* vc, const char* kn, const char* vn,
+                                                                  int64_t heads, int64_t head_units,
+                                                                  int64_t cache_head_bytes, int64_t dst_off) {
+  const int64_t u0 = (int64_t)blockIdx.x * APPEND_UNITS + threadIdx.x;
+  for (int64_t g = blockIdx.y; g < heads; g += gridDim.y) {
+    const int64_t src = g * head_units * 16;
+    const int64_t dst = g * cache_head_bytes + dst_off;
+#pragma unroll
+    for (int r = 0; r < APPEND_UNITS / APPEND_THREADS; ++r) {
+      const int64_t u = u0 + r * APPEND_THREADS;
+      if (u < head_units) {
+        const u32x4 k = *reinterpret_cast<const u32x4*>(kn + src + u * 16);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(vn + src + u * 16);
+        *reinterpret_cast<u32x4*>(kc + dst + u * 16) = k;
+        *reinterpret_cast<u32x4*>(vc + dst + u * 16) = v;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" int attn_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, int B, int H,
+                              int S_cap, int kv_len, int n_new, int D_h, int dtype, void* stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new) return ATTN_E_NULL;
+  if (B < 1 || H < 1 || S_cap < 1 || n_new < 1 || kv_len < 0 || D_h != HEAD_DIM) return ATTN_E_SHAPE;
+  if ((int64_t)kv_len + n_new > S_cap) return ATTN_E_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t row_bytes = (int64_t)HEAD_DIM * (dtype == ATTN_F32 ? 4 : 2);
+  if ((int64_t)S_cap > INT64_MAX / row_bytes / bh) return ATTN_E_SHAPE;
+  const uintptr_t mis = ((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) & 15u;
+  if (mis) return ATTN_E_ALIGN;
+  const uint64_t nc = (uint64_t)bh * S_cap * row_bytes, nn = (uint64_t)bh * n_new * row_bytes;
+  if (ranges_overlap(k_cache, nc, v_cache, nc) || ranges_overlap(k_cache, nc, k_new, nn) ||
+      ranges_overlap(k_cache, nc, v_new, nn) || ranges_overlap(v_cache, nc, k_new, nn) ||
+      ranges_overlap(v_cache, nc, v_new, nn))
+    return ATTN_E_OVERLAP;
+  int n_cu = 0;
+  const int dv = check_device(&n_cu);
+  if (dv != ATTN_OK) return dv;
+  const int64_t head_units = (int64_t)n_new * row_bytes / 16;
+  const int64_t bx = (head_units + APPEND_UNITS - 1) / APPEND_UNITS;
+  if (bx > INT32_MAX) return ATTN_E_SHAPE;
+  const int by = (int)std::min<int64_t>(bh, 65535);
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)bx, (unsigned)by), dim3(APPEND_THREADS), 0,
+                     static_cast<hipStream_t>(stream), static_cast<char*>(k_cache), static_cast<char*>(v_cache),
+                     static_cast<const char*>(k_new), static_cast<const char*>(v_new), bh, head_units,
+                     (int64_t)S_cap * row_bytes, (int64_t)kv_len * row_bytes);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
 
 extern "C" int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
                                 int S_kv, int D_h, int causal, float scale, int dtype, void* stream,
