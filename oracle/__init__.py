@@ -10,14 +10,19 @@ the explicit definition of Eq. A on the page "Shape-Aware Attention" (section
 causal rule "key j visible to query i iff j <= kv_len - S_q + i".  This module
 only marshals numpy arrays into it.
 
-``kv_append`` is the K/V cache append of the streaming use, a numpy slice
-assignment (no arithmetic).
+``attention_varlen`` is Eq. A for a batch of sequences of different lengths
+padded to one K/V capacity: per sequence, the same function on its own K/V
+prefix (a slice), with the bottom-right causal rule of that sequence's length
+and zeros for a query row that sees no key.  ``kv_append`` is the K/V cache
+append of the streaming use, a numpy slice assignment (no arithmetic).
 
 Parity status of each function is stated where it is tested (``tests/
 test_oracle_pins.py``): the attention function is pinned by closed forms,
 invariants, a library special case (torch CPU float64 SDPA with an explicit
-mask) and 50-digit brute force; ``kv_append`` by an element-by-element loop,
-two appends against one, and raw bit patterns; neither is "parity unpinned".
+mask) and 50-digit brute force; ``attention_varlen`` by SDPA with a
+per-sequence mask, padding that holds NaN, empty and single-key rows and
+batch permutations; ``kv_append`` by an element-by-element loop, two appends
+against one, and raw bit patterns; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -112,6 +117,38 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
                              int(n_rows), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_attn_f64: {ORACLE_ERRORS.get(rc, rc)}")
+    return o
+
+
+def attention_varlen(q, k, v, kv_lens, *, causal: bool = False, scale: float | None = None,
+                     threads: int = 0, lib=None) -> np.ndarray:
+    """Eq. A per sequence of a padded batch (key padding).  q: [B,H,S_q,D],
+    k/v: [B,H,S_kv,D]; sequence b attends only to its first L_b K/V rows,
+    L_b = kv_lens[b] clamped into [0, S_kv].  Causal: query row i of sequence
+    b sits at position L_b - S_q + i (bottom-right, as in ``attention``) and
+    sees keys j <= that position.  A row that sees no key -- L_b = 0, or a
+    causal row with L_b - S_q + i < 0 -- is zero: the pages define the softmax
+    only over a non-empty set, and zero is the empty weighted sum.  Each
+    sequence is ``attention`` on its slice k[b, :, :L_b] and on its query rows
+    from i0 = max(0, S_q - L_b) on (the rows that see a key; the slice keeps
+    their positions, since L_b - (S_q - i0) + (i - i0) = L_b - S_q + i).
+    Returns float64 [B,H,S_q,D]."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, S_q, D = q.shape
+    S_kv = k.shape[2]
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    if lens.size != B:
+        raise ValueError(f"kv_lens has {lens.size} values for a batch of {B}")
+    o = np.zeros((B, H, S_q, D), dtype=np.float64)
+    for b in range(B):
+        L = int(min(max(int(lens[b]), 0), S_kv))
+        if L == 0:
+            continue
+        i0 = max(0, S_q - L) if causal else 0
+        if i0 == S_q:
+            continue
+        o[b:b + 1, :, i0:] = attention(q[b:b + 1, :, i0:], k[b:b + 1, :, :L], v[b:b + 1, :, :L],
+                                       causal=causal, scale=scale, threads=threads, lib=lib)
     return o
 
 

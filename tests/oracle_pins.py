@@ -337,3 +337,119 @@ ALL_CHECKS = [
     check_shift_invariance, check_large_score_range, check_constant_values, check_value_scaling,
     check_permutations, check_row_subset, check_causal_prefix,
 ]
+
+
+# --------------------------------------------------------------------------
+# per-sequence key lengths (key padding): checks take ``attn_varlen``, a
+# callable with the signature of ``oracle.attention_varlen``
+# --------------------------------------------------------------------------
+def sdpa_varlen_reference(q, k, v, kv_lens, causal, scale):
+    """torch CPU float64 SDPA with one boolean mask per sequence, built from
+    the rule itself: key j is visible to row i of sequence b iff j < L_b and,
+    when causal, j <= L_b - S_q + i (L_b clamped into [0, S_kv]).  SDPA leaves
+    a row with no visible key undefined (NaN); such rows are set to zero, the
+    empty weighted sum."""
+    B, H, S_q, _ = q.shape
+    S_kv = k.shape[2]
+    mask = np.zeros((B, 1, S_q, S_kv), dtype=bool)
+    i = np.arange(S_q)[:, None]
+    j = np.arange(S_kv)[None, :]
+    for b in range(B):
+        L = min(max(int(kv_lens[b]), 0), S_kv)
+        vis = j < L
+        if causal:
+            vis = vis & (j <= L - S_q + i)
+        mask[b, 0] = vis
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))
+    out = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=torch.from_numpy(mask),
+                                                           scale=scale).numpy()
+    empty = ~mask.any(axis=3, keepdims=True)  # [B,1,S_q,1]
+    return np.where(np.broadcast_to(empty, out.shape), 0.0, out)
+
+
+VARLEN_SHAPES = [
+    # B, H, S_q, S_kv, D, causal, kv_lens, scale
+    (3, 2, 5, 9, 8, False, [9, 4, 1], None),
+    (3, 2, 5, 9, 8, True, [9, 5, 7], None),
+    (4, 1, 6, 10, 16, True, [3, 0, 10, 6], None),   # causal rows before the first key; an empty sequence
+    (2, 3, 7, 7, 64, False, [0, 7], -0.4),
+    (2, 2, 33, 70, 64, True, [70, 20], 0.3),
+    (5, 1, 4, 6, 3, False, [-2, 8, 6, 2, 1], 1.7),  # lengths outside [0, S_kv] are clamped
+]
+
+
+def _varlen_inputs(n, B, H, S_q, S_kv, D):
+    r = _rng(500 + n)
+    return _randn(r, (B, H, S_q, D)), _randn(r, (B, H, S_kv, D)), _randn(r, (B, H, S_kv, D))
+
+
+def check_varlen_sdpa(attn_varlen):
+    for n, (B, H, S_q, S_kv, D, causal, lens, scale) in enumerate(VARLEN_SHAPES):
+        q, k, v = _varlen_inputs(n, B, H, S_q, S_kv, D)
+        sc = 1.0 / math.sqrt(D) if scale is None else scale
+        got = attn_varlen(q, k, v, lens, causal=causal, scale=sc)
+        ref = sdpa_varlen_reference(q, k, v, lens, causal, sc)
+        assert got.shape == ref.shape, f"varlen shape {n}: {got.shape} vs {ref.shape}"
+        assert np.all(np.isfinite(got)), f"varlen shape {n}: non-finite output"
+        err = np.max(np.abs(got - ref))
+        assert err <= 1e-12, f"varlen SDPA shape {n}: max err {err}"
+
+
+def check_varlen_padding_ignored(attn_varlen):
+    # Rows at or past a sequence's length never enter its result: NaN there
+    # changes nothing.
+    for n, (B, H, S_q, S_kv, D, causal, lens, scale) in enumerate(VARLEN_SHAPES):
+        q, k, v = _varlen_inputs(n, B, H, S_q, S_kv, D)
+        kp, vp = k.copy(), v.copy()
+        for b in range(B):
+            L = min(max(lens[b], 0), S_kv)
+            kp[b, :, L:] = np.nan
+            vp[b, :, L:] = np.nan
+        a = attn_varlen(q, k, v, lens, causal=causal, scale=scale)
+        c = attn_varlen(q, kp, vp, lens, causal=causal, scale=scale)
+        assert np.array_equal(a, c), f"varlen shape {n}: padding rows change the result"
+
+
+def check_varlen_empty_and_single_key_rows(attn_varlen):
+    # L = 0: every row is zero.  Causal with L < S_q: rows i < S_q - L see no
+    # key (zero); row S_q - L sees key 0 alone and returns V[0] exactly.
+    B, H, S_q, S_kv, D = 3, 2, 8, 12, 5
+    q, k, v = _varlen_inputs(99, B, H, S_q, S_kv, D)
+    lens = [0, 3, 12]
+    o = attn_varlen(q, k, v, lens, causal=True, scale=0.8)
+    assert np.all(o[0] == 0.0), "an empty sequence must give zeros"
+    assert np.all(o[1, :, :S_q - 3] == 0.0), "causal rows before the first key must be zero"
+    assert np.array_equal(o[1, :, S_q - 3], v[1, :, 0].astype(np.float64)), "a row that sees one key returns its value"
+    assert np.all(o[1, :, S_q - 3 + 1:] != 0.0)
+    o = attn_varlen(q, k, v, lens, causal=False, scale=0.8)
+    assert np.all(o[0] == 0.0)
+    assert np.all(np.any(o[1] != 0.0, axis=-1)), "non-causal rows of a non-empty sequence see every key"
+
+
+def check_varlen_full_lengths_equal_attention(attn_varlen):
+    # All lengths at capacity: the padded batch is the plain batch (compared
+    # with the directly masked library result, not with the oracle).
+    B, H, S_q, S_kv, D = 2, 2, 6, 9, 8
+    q, k, v = _varlen_inputs(77, B, H, S_q, S_kv, D)
+    for causal in (False, True):
+        got = attn_varlen(q, k, v, [S_kv] * B, causal=causal, scale=0.5)
+        ref = sdpa_reference(q, k, v, causal, 0.5)
+        assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def check_varlen_batch_permutation(attn_varlen):
+    # Reordering the sequences (with their lengths) reorders the results.
+    B, H, S_q, S_kv, D = 4, 2, 5, 8, 4
+    q, k, v = _varlen_inputs(55, B, H, S_q, S_kv, D)
+    lens = np.array([8, 2, 5, 0])
+    perm = np.array([2, 0, 3, 1])
+    for causal in (False, True):
+        a = attn_varlen(q, k, v, lens, causal=causal, scale=0.9)
+        c = attn_varlen(q[perm], k[perm], v[perm], lens[perm], causal=causal, scale=0.9)
+        assert np.array_equal(a[perm], c), "batch permutation"
+
+
+VARLEN_CHECKS = [
+    check_varlen_sdpa, check_varlen_padding_ignored, check_varlen_empty_and_single_key_rows,
+    check_varlen_full_lengths_equal_attention, check_varlen_batch_permutation,
+]

@@ -62,3 +62,38 @@ def test_mutant_is_caught(source, name, old, new):
                 caught.append(check.__name__)
                 break
         assert caught, f"mutant {name} passed every pin"
+
+
+# The per-sequence layer of oracle.attention_varlen (Python over the C
+# function): each mutant plants one slip in a copy of its source text, which is
+# executed in the oracle module's namespace; the varlen pins must catch it.
+VARLEN_MUTANTS = [
+    ("first_length_for_all", "int(lens[b])", "int(lens[0])"),
+    ("not_clamped_low", "min(max(int(lens[b]), 0), S_kv)", "min(int(lens[b]), S_kv)"),
+    ("causal_start_off_by_one", "max(0, S_q - L) if causal", "max(0, S_q - L + 1) if causal"),
+    ("causal_top_left_rows", "o[b:b + 1, :, i0:] = attention(q[b:b + 1, :, i0:]",
+     "o[b:b + 1, :, i0:] = attention(q[b:b + 1, :, :S_q - i0]"),
+    ("whole_cache_read", "k[b:b + 1, :, :L], v[b:b + 1, :, :L]", "k[b:b + 1], v[b:b + 1]"),
+    ("empty_rows_not_zero", "o = np.zeros((B, H, S_q, D), dtype=np.float64)",
+     "o = np.full((B, H, S_q, D), np.nan)"),
+    ("non_causal_inner_call", "causal=causal, scale=scale, threads", "causal=False, scale=scale, threads"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", VARLEN_MUTANTS, ids=[m[0] for m in VARLEN_MUTANTS])
+def test_varlen_mutant_is_caught(name, old, new):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(oracle.attention_varlen))
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), ns)
+    mutant = ns["attention_varlen"]
+    caught = []
+    for check in pins.VARLEN_CHECKS:
+        try:
+            check(mutant)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"varlen mutant {name} passed every pin"

@@ -18,6 +18,11 @@ def test_pin(check):
     check(oracle.attention)
 
 
+@pytest.mark.parametrize("check", pins.VARLEN_CHECKS, ids=lambda f: f.__name__)
+def test_varlen_pin(check):
+    check(oracle.attention_varlen)
+
+
 def _heads(x, n):
     return x[:1, :n].contiguous()
 

@@ -148,3 +148,19 @@ def multi_seed_list(count: int = 40, base: int = 100):
     Attention", section "Challenges we ran into", where one configuration
     passed on only some seeds)."""
     return list(range(base, base + count))
+
+
+def varlen_lengths(B: int, S_kv: int, seed: int, low: float = 0.25, edges: bool = True) -> torch.Tensor:
+    """int32 [B] per-sequence key lengths for a batch padded to S_kv keys: the
+    pages give no length mix, so lengths are uniform on [ceil(low*S_kv), S_kv]
+    (seeded), and with ``edges`` the first few sequences take the boundary
+    lengths S_kv, 1, 0 and one past a 64-key tile (where B allows)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    lo = max(1, -(-int(low * S_kv * 1000) // 1000))
+    lens = torch.randint(lo, S_kv + 1, (B,), generator=g, dtype=torch.int64)
+    if edges:
+        for i, L in enumerate((S_kv, 1, 0, min(S_kv, 65))):
+            if i < B:
+                lens[i] = L
+    return lens.to(torch.int32)
