@@ -42,8 +42,12 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: enough for about 0.5 s of GPU time, 10 .. 20000)")
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="the timed steps are split into this many back-to-back repeats (median reported)")
+    ap.add_argument("--no-aa", action="store_true", help="skip the A/A control (a second timing of the same steps)")
     ap.add_argument("--workload", default="c2_mha_s512")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +57,9 @@ def parse():
                     help="chunked workloads: one step runs every query window in order, appending the "
                          "window's K/V rows to a cache (attn_kv_append) and attending its queries to the "
                          "grown cache (attn_fwd_chunked)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="attn_fwd_varlen with per-sequence key lengths drawn uniform on [S_kv/4, S_kv] "
+                         "(seeded); value counts only the visible (row, key) pairs")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-mb", type=float, default=None,
@@ -85,9 +92,26 @@ def copy_calibration(args):
     print(json.dumps(line), flush=True)
 
 
-def roofline_for(w, dtype, sec_per_call):
-    flops = w.flops()
-    nbytes = w.bytes(dtype)
+def varlen_work(w, lens, dtype):
+    """Counted FLOPs (4*D per visible (row, key) pair) and algorithmic HBM
+    bytes (Q and O once, each sequence's first L_b K/V rows once) of one
+    attn_fwd_varlen call with per-sequence lengths `lens`."""
+    import torch
+    e = torch.finfo(getattr(torch, {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}[dtype])).bits // 8
+    pairs, kv_rows = 0, 0
+    for L in (min(max(int(x), 0), w.S_kv) for x in lens):
+        kv_rows += L
+        if w.causal:  # row i sees min(L, max(0, L - S_q + i + 1)) keys
+            pairs += sum(min(L, max(0, L - w.S_q + i + 1)) for i in range(w.S_q))
+        else:
+            pairs += w.S_q * L
+    flops = 4.0 * w.D * pairs * w.H
+    nbytes = (2 * w.S_q * w.B + 2 * kv_rows) * w.D * e * w.H
+    return flops, nbytes
+
+
+def roofline_for(w, dtype, sec_per_call, work=None):
+    flops, nbytes = work if work is not None else (w.flops(), w.bytes(dtype))
     t_mfma = flops / (PEAK[f"mfma_{dtype}"] * 1e12)
     t_hbm = nbytes / (PEAK["hbm"] * 1e9)
     if t_hbm > t_mfma:
@@ -100,19 +124,31 @@ def roofline_for(w, dtype, sec_per_call):
             "frac": round(ach / pk, 4), "traffic": None}
 
 
+def code_key(path):
+    """sha256 prefix of a C++/HIP source with its comments removed and its
+    whitespace collapsed: it changes when the code changes, not when a comment
+    does.  (The kernel source holds no string literal with a comment marker.)"""
+    import hashlib
+    import re
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
+
+
 def measured_traffic(workload, dtype):
     """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
-    or None when there is no entry or the kernel source changed since."""
-    import hashlib
+    or None when there is no entry or the kernel code changed since."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             t = json.load(f)
-        with open(os.path.join(ROOT, t["kernel_source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        key = code_key(os.path.join(ROOT, t["kernel_source"]))
     except (OSError, KeyError, ValueError):
         return None
     e = t.get("entries", {}).get(f"{workload}/{dtype}")
-    if e is None or sha != t.get("source_sha256_16"):
+    if e is None or key != t.get("code_sha256_16"):
         return None
     return e["traffic_bytes"]
 
@@ -153,10 +189,65 @@ def cpu_baseline(w, dtype, budget_s):
     shift = w.S_kv - w.S_q
     vis = (np.minimum(r + shift + 1, w.S_kv) if w.causal else np.full(len(r), w.S_kv)).sum()
     flops = 4.0 * w.D * float(vis) * heads
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    rate = flops / el
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} head(s) x {len(r)} query-row evaluations (rows of {w.S_q}, in random order) "
                       f"({flops / 1e9:.2f} GFLOP counted, {el:.1f} s, fp64)",
-            "seconds": round(el, 3)}
+            "seconds": round(el, 3), "gflop_per_s": round(rate / 1e9, 3),
+            "us_per_row_per_head": round(el / (len(r) * heads) * 1e6, 3),
+            "extrapolated_full_workload_s": round(w.flops() / rate, 1),
+            "extrapolation_note": "counted FLOPs of the whole workload / the sample's rate (not measured)"}
+
+
+def gpu_clock_mhz(dev, n_wg=256, iters=4096):
+    """Shader clock (MHz) while a short busy kernel runs: median over waves of
+    100 MHz * shader cycles / reference ticks (attn_clock_probe).  None if the
+    probe library is missing."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "transformer_attention_04_amd", "libattn_clock.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.attn_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    out = torch.zeros(2 * n_wg, dtype=torch.int64, device=dev)
+    st = lib.attn_clock_probe(out.data_ptr(), n_wg, iters, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    if st != 0:
+        return None
+    torch.cuda.synchronize()
+    c = out.view(n_wg, 2).cpu().double()
+    mhz = 100.0 * c[:, 0] / c[:, 1].clamp(min=1)
+    return round(float(mhz.median()), 1)
+
+
+def environment(dev):
+    """What the numbers were measured on: versions, GPU, host CPU, build."""
+    import platform
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    info = {}
+    try:
+        with open(os.path.join(ROOT, "transformer_attention_04_amd", "build_info.json")) as f:
+            info = json.load(f)
+    except (OSError, ValueError):
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "cu": props.multi_processor_count,
+            "torch": torch.__version__, "hip": torch.version.hip, "python": platform.python_version(),
+            "host_cpu": cpu, "host_cores": len(os.sched_getaffinity(0)),
+            "git_rev": info.get("git_rev"), "tree_modified_at_build": info.get("tree_modified"),
+            "hipcc": info.get("hipcc")}
+
+
+def split_steps(k, r):
+    """Split k steps into r back-to-back repeats (sizes differ by at most one)."""
+    r = max(1, min(r, k))
+    return [k // r + (1 if i < k % r else 0) for i in range(r)]
 
 
 def main():
@@ -192,6 +283,16 @@ def main():
                 q, k, v = q0.clone(), k0.clone(), v0.clone()
             sets.append((q, k, v, torch.empty_like(q)))
     chunk = w.chunk
+    work = None
+    if args.varlen:
+        if chunk or args.stream:
+            print("--varlen takes a single-call workload", file=sys.stderr)
+            sys.exit(2)
+        lens_cpu = W.varlen_lengths(w.B, w.S_kv, seed=w.seed + 900, edges=False)
+        lens = lens_cpu.to(dev)
+        work = varlen_work(w, lens_cpu.tolist(), dtype)
+        log(f"[bench] varlen: lengths {lens_cpu.tolist()[:8]}..., "
+            f"{work[0] / w.flops():.3f} of the full-length work")
     if args.stream:
         if not chunk:
             print("--stream needs a chunked workload", file=sys.stderr)
@@ -214,7 +315,9 @@ def main():
                 A.attn_fwd_chunked(qw, kc, vc, chunk=chunk, kv_len=kv, causal=w.causal, scale=w.scale, out=ow)
             return
         q, k, v, o = sets[i % len(sets)]
-        if chunk:
+        if args.varlen:
+            A.attn_fwd_varlen(q, k, v, lens, causal=w.causal, scale=w.scale, out=o)
+        elif chunk:
             A.attn_fwd_chunked(q, k, v, chunk=chunk, causal=w.causal, scale=w.scale, out=o)
         else:
             A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o)
@@ -222,35 +325,67 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    graph = None
+    stream = torch.cuda.current_stream(dev)
+    if args.steps is None:  # about 0.5 s of GPU time, from a short eager estimate
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_est = 3 if args.stream or chunk else 20
+        e0.record(stream)
+        for i in range(n_est):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        est = e0.elapsed_time(e1) / n_est
+        args.steps = int(min(20000, max(10, math.ceil(500.0 / max(est, 1e-3)))))
+        if args.stream or chunk:
+            args.steps = min(args.steps, 5)
+        log(f"[bench] ~{est * 1e3:.1f} us per eager step: timing {args.steps} steps")
+    sizes = split_steps(args.steps, args.repeats)
+    graphs = {}
     if not args.eager:
-        # The K timed steps are captured once into a HIP graph and replayed as
-        # one launch, so host-side call overhead does not leave the GPU idle
+        # The timed steps are captured into HIP graphs (one per repeat size)
+        # and replayed, so host-side call overhead does not leave the GPU idle
         # between the short kernels.  The kernels and their inputs are the
         # same as in eager mode.
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        graph.replay()  # one untimed replay
+        for n in sorted(set(sizes)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    step(i)
+            g.replay()  # one untimed replay
+            graphs[n] = g
         torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed():
+        """Exactly args.steps steps, in back-to-back repeats, between HIP events
+        on the launch stream.  Returns (total ms, [ms per step of each repeat])."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
+        ev[0].record(stream)
+        for r, n in enumerate(sizes):
+            if graphs:
+                graphs[n].replay()
+            else:
+                for i in range(n):
+                    step(i)
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[-1]), [ev[r].elapsed_time(ev[r + 1]) / n for r, n in enumerate(sizes)]
+
+    clk0 = gpu_clock_mhz(dev)
     t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    total_ms, rep_ms = timed()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    clk1 = gpu_clock_mhz(dev)
+    ms = total_ms / args.steps
     sec = ms / 1e3
-    tflops = w.flops() / sec / 1e12
-    log(f"[bench] {ms * 1e3:.2f} us/call, {tflops:.2f} TFLOP/s, wall {wall:.3f} s")
+    tflops = (work[0] if work else w.flops()) / sec / 1e12
+    med = sorted(rep_ms)[len(rep_ms) // 2]
+    log(f"[bench] {ms * 1e3:.2f} us/call (median of {len(rep_ms)} repeats {med * 1e3:.2f}), "
+        f"{tflops:.2f} TFLOP/s, wall {wall:.3f} s, clock {clk0} -> {clk1} MHz")
+    aa = None
+    if not args.no_aa:  # A/A control: the same steps timed again in this process
+        total2, _ = timed()
+        aa = round(total2 / total_ms, 4)
+        log(f"[bench] A/A: second timing / first = {aa}")
 
     line = {
         "metric": METRIC, "value": round(tflops, 4), "unit": "TFLOP/s", "n_gpus": 1,
@@ -259,11 +394,23 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_q": w.S_q, "S_kv": w.S_kv, "D_h": w.D,
                    "causal": w.causal, "chunk": w.chunk, "rotating_sets": 1 if args.stream else len(sets),
-                   "mode": "stream: append + attend per window" if args.stream else "single call",
-                   "launch": "eager" if graph is None else "hip_graph_replay"},
-        "roofline": roofline_for(w, dtype, sec),
+                   "mode": ("stream: append + attend per window" if args.stream else
+                            "varlen: per-sequence key lengths uniform on [S_kv/4, S_kv], visible pairs counted"
+                            if args.varlen else "single call"),
+                   "launch": "hip_graph_replay" if graphs else "eager"},
+        "roofline": roofline_for(w, dtype, sec, work),
+        "timing": {"repeats": len(rep_ms), "steps_per_repeat": sizes,
+                   "ms_per_step_each_repeat": [round(x, 6) for x in rep_ms],
+                   "median_ms_per_step": round(med, 6),
+                   "gpu_clock_mhz": {"before": clk0, "after": clk1,
+                                     "after_over_before": round(clk1 / clk0, 4) if clk0 and clk1 else None,
+                                     "below_85pct": (clk1 < 0.85 * clk0) if clk0 and clk1 else None},
+                   "aa_ratio": aa},
+        "environment": environment(dev),
     }
-    line["roofline"]["traffic"] = None if args.stream else measured_traffic(w.name, dtype)
+    if args.varlen:
+        line["config"]["kv_lens"] = lens_cpu.tolist()
+    line["roofline"]["traffic"] = None if (args.stream or args.varlen) else measured_traffic(w.name, dtype)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)

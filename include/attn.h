@@ -124,6 +124,28 @@ int attn_fwd_chunked(const void *q, const void *k, const void *v, void *o,
                      int chunk, int kv_len);
 
 /*
+ * attn_fwd_varlen -- attn_fwd for a batch of sequences of different lengths
+ * padded to S_kv keys: sequence b (every head h) attends only to its first
+ * kv_lens[b] K/V rows (key padding; the case the causal kernel of the page
+ * "GPU Kernel for a Transformer Layer", section "How we built it", left to a
+ * library call).  Causal masking is bottom-right per sequence:
+ * query row i sits at position kv_lens[b] - S_q + i; a row that sees no key
+ * (kv_lens[b] = 0, or a causal row before the sequence's first key) gets
+ * zeros.
+ *   kv_lens : DEVICE pointer to B int32 values, 4-byte aligned; each value is
+ *             clamped into [0, S_kv] (rows past S_kv are never read).
+ *   Other arguments as attn_fwd.  Rows of K/V at or past kv_lens[b] are never
+ *   read.  The key split follows the same rule as attn_fwd.
+ * Errors as attn_fwd, except that causal calls with S_q > a sequence's length
+ * are allowed; ATTN_E_NULL also for a NULL kv_lens, ATTN_E_ALIGN for a
+ * misaligned one.
+ */
+int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o,
+                    int B, int H, int S_q, int S_kv, int D_h,
+                    int causal, float scale, int dtype, void *stream,
+                    const int *kv_lens);
+
+/*
  * attn_kv_append -- write n_new new key and value rows into a K/V cache at
  * row kv_len of every (b, h): the append step of a stream of bounded query
  * windows against a growing key/value cache (page "Roofline", section "How

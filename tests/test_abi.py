@@ -194,3 +194,39 @@ def test_append_valid_call_without_gpu_reports_device():
         pytest.skip("a GPU is present")
     assert call_append() == 9
     assert call_append(kv_len=0, n=100, dtype=0) == 9   # fills the whole cache
+
+
+# attn_fwd_varlen: per-sequence key lengths in a device array (a fake aligned
+# address here: validation never reads it).
+LENS = 0x500000
+GOOD_VARLEN = dict(q=Q, k=K, v=V, o=O, B=2, H=3, S_q=100, S_kv=120, D=64, causal=1, scale=0.125, dtype=2,
+                   lens=LENS)
+
+
+def call_varlen(**kw):
+    a = dict(GOOD_VARLEN, **kw)
+    return A.lib.attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["S_q"], a["S_kv"], a["D"],
+                                 a["causal"], a["scale"], a["dtype"], None, a["lens"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=0), 1), (dict(q=0), 1), (dict(o=0), 1),
+    (dict(B=0), 2), (dict(S_kv=0), 2), (dict(D=128), 2), (dict(B=1 << 20, H=1 << 12), 2),
+    (dict(dtype=4), 3), (dict(scale=float("nan")), 4),
+    (dict(lens=LENS + 2), 7), (dict(lens=LENS + 1), 7), (dict(k=K + 8), 7),
+    (dict(o=V), 8),
+])
+def test_varlen_invalid_arguments_return_their_code(kw, code):
+    assert call_varlen(**kw) == code
+
+
+def test_varlen_valid_call_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_varlen() == 9
+    # A causal call with more query rows than keys passes validation: rows
+    # that see no key are defined (zeros), unlike attn_fwd's ATTN_E_CAUSAL.
+    assert call_varlen(S_q=200, S_kv=120) == 9
+    assert call_varlen(lens=LENS + 4, dtype=0, causal=0) == 9   # 4-byte alignment is enough for the lengths
+

@@ -7,6 +7,7 @@ built, importing this package raises.
 
     attn_fwd(q, k, v, causal=False, scale=None)            -> o
     attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o
+    attn_fwd_varlen(q, k, v, kv_lens, causal=False, ...)     -> o
     attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len)   -> kv_len + n
     attn_strerror(status)                                    -> str
 
@@ -29,7 +30,7 @@ STATUS = {
     5: "ATTN_E_CAUSAL", 6: "ATTN_E_CHUNK", 7: "ATTN_E_ALIGN", 8: "ATTN_E_OVERLAP",
     9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_kv_append", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
+EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_kv_append", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
 
 
 class AttnError(RuntimeError):
@@ -48,6 +49,8 @@ def _load(path: str = LIB_PATH):
     lib.attn_fwd.restype = i
     lib.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, i, i]
     lib.attn_fwd_chunked.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, vp]
+    lib.attn_fwd_varlen.restype = i
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_kv_append.restype = i
     lib.attn_strerror.argtypes = [i]
@@ -147,6 +150,29 @@ def attn_fwd_chunked(q, k, v, chunk: int, kv_len: int | None = None, causal: boo
     st = _call(lib.attn_fwd_chunked, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                B, H, S_q, S_kv, D, int(bool(causal)), float(scale),
                _dtype_code(q), _stream_ptr(dev, stream), int(chunk), int(kv_len))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return o
+
+
+def attn_fwd_varlen(q, k, v, kv_lens, causal: bool = False, scale: float | None = None, out=None, stream=None):
+    """attn_fwd with per-sequence valid key lengths: sequence b attends to its
+    first kv_lens[b] K/V rows (kv_lens: int32 GPU tensor [B]; see attn_fwd_varlen
+    in include/attn.h)."""
+    torch = _t()
+    B, H, S_q, S_kv, D = _check(q, k, v)
+    if (kv_lens.dtype != torch.int32 or kv_lens.dim() != 1 or kv_lens.shape[0] != B or not kv_lens.is_contiguous()
+            or kv_lens.device != q.device):
+        raise ValueError("kv_lens must be a contiguous int32 tensor [B] on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    dev = q.device
+    st = _call(lib.attn_fwd_varlen, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+               B, H, S_q, S_kv, D, int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(dev, stream),
+               kv_lens.data_ptr())
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o

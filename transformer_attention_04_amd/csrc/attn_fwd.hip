@@ -147,6 +147,9 @@ struct Params {
   float c;          // |scale| * log2(e)
   unsigned q_flip;  // XOR mask on Q's 32-bit words: sign flip for negative scale
   Sched s;
+  const int* kv_lens;  // per-sequence valid K/V rows (device, B values) or null: kv_len for all
+  int H;
+  int S_kv;
 };
 
 __device__ __forceinline__ float other_half(float x) {
@@ -558,7 +561,10 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 //
 // Pipeline: a stage holds KS consecutive 64-key tiles of K, then of V.  With
 // three stages two stages are in flight while one is computed; with two, one.
-template <typename T, bool CAUSAL, int KS>
+//
+// VARLEN: each sequence has its own key length, read from p.kv_lens (key
+// padding); a row that then sees no key gets zeros.
+template <typename T, bool CAUSAL, int KS, bool VARLEN>
 __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2 : 1)
     attn_fwd_kernel(Params<T> p) {
   constexpr bool F32 = sizeof(T) == 4;
@@ -594,9 +600,12 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   const T* vh_ptr = p.v + (int64_t)head * p.kv_head_stride;
   T* oh = p.o + (int64_t)head * p.q_head_stride;
 
-  const int kv_len = p.kv_len;
+  // Valid K/V rows of this head's sequence: kv_len, or its own length
+  // clamped into the cache (a row that sees no key gets zeros).
+  const int kv_len = VARLEN ? min(max(p.kv_lens[head / p.H], 0), p.S_kv) : p.kv_len;
   const int shift = kv_len - p.S_q;  // absolute position of query row r is r + shift
-  const int kv_end = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
+  const int kv_end0 = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
+  const int kv_end = VARLEN ? max(0, kv_end0) : kv_end0;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const int n_super = (n_tiles + KS - 1) / KS;
 
@@ -1068,17 +1077,26 @@ Sched make_sched(int B, int H, int S_q, int chunk, int kv_len, int causal) {
   return s;
 }
 
+template <typename T, int KS, bool VARLEN>
+void launch_kernel_v(const Params<T>& p, int grid, int causal, hipStream_t stream) {
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS, VARLEN>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS, VARLEN>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+}
+
 template <typename T, int KS>
 void launch_kernel(const Params<T>& p, int grid, int causal, hipStream_t stream) {
-  if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+  if (p.kv_lens)
+    launch_kernel_v<T, KS, true>(p, grid, causal, stream);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+    launch_kernel_v<T, KS, false>(p, grid, causal, stream);
 }
 
 template <typename T>
 int launch_typed(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
-                 int causal, float scale, hipStream_t stream, int chunk, int kv_len, int n_cu) {
+                 int causal, float scale, hipStream_t stream, int chunk, int kv_len, int n_cu,
+                 const int* kv_lens = nullptr) {
   Params<T> p;
   p.q = static_cast<const T*>(q);
   p.k = static_cast<const T*>(k);
@@ -1088,6 +1106,9 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   p.kv_head_stride = (int64_t)S_kv * HEAD_DIM;
   p.S_q = S_q;
   p.kv_len = kv_len;
+  p.kv_lens = kv_lens;
+  p.H = H;
+  p.S_kv = S_kv;
   // |scale| * log2(e), at least 1e-30 so that a masked score (-inf) always
   // exponentiates to 0; for scale = 0 every visible probability is still
   // exp2(~1e-27) = 1 exactly in fp32.
@@ -1191,6 +1212,29 @@ extern "C" int attn_fwd_chunked(const void* q, const void* k, const void* v, voi
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
                         int D_h, int causal, float scale, int dtype, void* stream) {
   return attn_fwd_chunked(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, stream, S_q, S_kv);
+}
+
+extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
+                               int S_kv, int D_h, int causal, float scale, int dtype, void* stream,
+                               const int* kv_lens) {
+  if (!kv_lens) return ATTN_E_NULL;
+  if ((uintptr_t)kv_lens & 3u) return ATTN_E_ALIGN;
+  // Checked as a non-causal call over the whole cache: with per-sequence
+  // lengths a causal row may see no key (it gets zeros).
+  const int st = validate(q, k, v, o, B, H, S_q, S_kv, D_h, 0, scale, dtype, S_q, S_kv);
+  if (st != ATTN_OK) return st;
+  int n_cu = 0;
+  const int dv = check_device(&n_cu);
+  if (dv != ATTN_OK) return dv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case ATTN_F32:
+      return launch_typed<float>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, S_kv, n_cu, kv_lens);
+    case ATTN_F16:
+      return launch_typed<_Float16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, S_kv, n_cu, kv_lens);
+    default:
+      return launch_typed<__bf16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, S_kv, n_cu, kv_lens);
+  }
 }
 
 extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int* grid) {
