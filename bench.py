@@ -60,6 +60,11 @@ def parse():
     ap.add_argument("--varlen", action="store_true",
                     help="attn_fwd_varlen with per-sequence key lengths drawn uniform on [S_kv/4, S_kv] "
                          "(seeded); value counts only the visible (row, key) pairs")
+    ap.add_argument("--decode", type=int, default=None, metavar="R",
+                    help="R query rows (the last R positions) against the workload's whole K/V cache through "
+                         "attn_fwd_splitkv (keys split over workgroup ranges and merged)")
+    ap.add_argument("--n-split", type=int, default=0,
+                    help="key ranges for --decode (0: attn_splitkv_choose for this GPU)")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-mb", type=float, default=None,
@@ -159,7 +164,7 @@ def cpu_baseline(w, dtype, budget_s):
     import oracle
     import workloads as W
     threads = len(os.sched_getaffinity(0))
-    small = w.S_q * w.S_kv * w.B * w.H <= (1 << 27)
+    small = w.S_q * w.S_kv * w.B * w.H <= (1 << 27) and w.B * w.H * (w.S_q + 2 * w.S_kv) * w.D <= (1 << 27)
     if small:
         q, k, v = W.make_inputs(w, dtype)
     else:  # one (b,h) head of the workload's shape
@@ -265,13 +270,20 @@ def main():
 
     w = W.BY_NAME[args.workload]
     dtype = args.dtype or w.dtypes[0]
+    if args.decode:
+        if args.varlen or args.stream:
+            print("--decode takes neither --varlen nor --stream", file=sys.stderr)
+            sys.exit(2)
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}_decode{args.decode}", S_q=args.decode, chunk=None,
+                                sample_rows=None)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     footprint = w.bytes(dtype)
     n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
     log(f"[bench] workload {w.name} dtype {dtype}: {footprint / 1e6:.1f} MB per set, {n_sets} sets")
     sets = []
-    if w.S_q * w.S_kv * w.B * w.H > (1 << 32):  # long context: draw on the device
+    if w.S_q * w.S_kv * w.B * w.H > (1 << 32) or w.B * w.H * w.S_kv * w.D > (1 << 28):  # large: draw on the device
         q, k, v = W.make_device_inputs(w, dtype, dev)
         sets.append((q, k, v, torch.empty_like(q)))
     else:
@@ -284,6 +296,15 @@ def main():
             sets.append((q, k, v, torch.empty_like(q)))
     chunk = w.chunk
     work = None
+    if args.decode:
+        R, kvl = w.S_q, w.S_kv
+        pairs = sum(min(kvl, max(0, kvl - R + i + 1)) for i in range(R)) if w.causal else R * kvl
+        e = torch.finfo(W.DTYPES[dtype]).bits // 8
+        work = (4.0 * w.D * pairs * w.B * w.H, (2 * R + 2 * kvl) * w.D * e * w.B * w.H)
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        n_split = args.n_split or A.splitkv_choose(w.B, w.H, R, kvl, n_cu)
+        ws = torch.empty(max(16, A.splitkv_workspace_bytes(w.B, w.H, R, n_split)), dtype=torch.uint8, device=dev)
+        log(f"[bench] decode: {R} row(s) x {kvl} keys per head, n_split {n_split}")
     if args.varlen:
         if chunk or args.stream:
             print("--varlen takes a single-call workload", file=sys.stderr)
@@ -315,7 +336,9 @@ def main():
                 A.attn_fwd_chunked(qw, kc, vc, chunk=chunk, kv_len=kv, causal=w.causal, scale=w.scale, out=ow)
             return
         q, k, v, o = sets[i % len(sets)]
-        if args.varlen:
+        if args.decode:
+            A.attn_fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, n_split=n_split, out=o, workspace=ws)
+        elif args.varlen:
             A.attn_fwd_varlen(q, k, v, lens, causal=w.causal, scale=w.scale, out=o)
         elif chunk:
             A.attn_fwd_chunked(q, k, v, chunk=chunk, causal=w.causal, scale=w.scale, out=o)
@@ -394,7 +417,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_q": w.S_q, "S_kv": w.S_kv, "D_h": w.D,
                    "causal": w.causal, "chunk": w.chunk, "rotating_sets": 1 if args.stream else len(sets),
-                   "mode": ("stream: append + attend per window" if args.stream else
+                   "mode": (f"decode: {w.S_q} query row(s) against the whole cache, keys split over "
+                            f"{n_split} workgroup range(s) (attn_fwd_splitkv)" if args.decode else
+                            "stream: append + attend per window" if args.stream else
                             "varlen: per-sequence key lengths uniform on [S_kv/4, S_kv], visible pairs counted"
                             if args.varlen else "single call"),
                    "launch": "hip_graph_replay" if graphs else "eager"},
@@ -410,7 +435,8 @@ def main():
     }
     if args.varlen:
         line["config"]["kv_lens"] = lens_cpu.tolist()
-    line["roofline"]["traffic"] = None if (args.stream or args.varlen) else measured_traffic(w.name, dtype)
+    line["roofline"]["traffic"] = (None if (args.stream or args.varlen or args.decode)
+                                   else measured_traffic(w.name, dtype))
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)

@@ -52,6 +52,8 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -73,7 +75,9 @@ enum attn_status {
     ATTN_E_ALIGN = 7,    /* a base pointer is not 16-byte aligned */
     ATTN_E_OVERLAP = 8,  /* o overlaps q, k or v */
     ATTN_E_DEVICE = 9,   /* no current HIP device, or it is not gfx950 */
-    ATTN_E_LAUNCH = 10   /* the kernel launch reported an error */
+    ATTN_E_LAUNCH = 10,  /* the kernel launch reported an error */
+    ATTN_E_SPLIT = 11,   /* n_split outside [1, 1024], or the split grid exceeds 2^31 - 1 workgroups */
+    ATTN_E_WORKSPACE = 12 /* workspace NULL, not 16-byte aligned, smaller than required, or overlapping q/k/v/o */
 };
 
 /*
@@ -144,6 +148,48 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o,
                     int B, int H, int S_q, int S_kv, int D_h,
                     int causal, float scale, int dtype, void *stream,
                     const int *kv_lens);
+
+/*
+ * attn_fwd_splitkv -- attn_fwd_chunked with one query window (chunk = S_q)
+ * whose keys are also split across workgroups: the first kv_len K/V rows are
+ * cut into n_split ranges of whole 64-key tiles; each range is attended on its
+ * own with the online-softmax state of the page "GPU Kernel for a Transformer
+ * Layer" (section "What we learned": running maximum, running sum, rescaled
+ * accumulator), and a second kernel merges the ranges' states exactly as the
+ * online update merges two blocks: with M the largest offset, O = sum
+ * 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s.  This is the regime of few query
+ * tiles against a long cache (a decode step of the growing cache of the page
+ * "Roofline", section "How we built it"; small batches, where the page "GPU
+ * Kernel for a Transformer Layer", section "What we learned", loses to a
+ * library call): more workgroups than query tiles.
+ *   kv_len     : valid K/V rows, 1 <= kv_len <= S_kv (as attn_fwd_chunked).
+ *   n_split    : 1 .. 1024 key ranges (attn_splitkv_choose picks one); 1 runs
+ *                attn_fwd_chunked(..., S_q, kv_len) and needs no workspace.
+ *   workspace  : DEVICE memory of at least attn_splitkv_workspace_bytes(B, H,
+ *                S_q, n_split) bytes, 16-byte aligned, not overlapping any
+ *                tensor; owned by the caller, overwritten by every call (calls
+ *                that overlap in time must not share one).  Holds fp32 partial
+ *                states only; nothing needs clearing between calls.
+ * Same result as attn_fwd_chunked up to fp32 rounding order (the ranges are
+ * summed in a different order).  Errors: as attn_fwd_chunked; ATTN_E_SPLIT;
+ * ATTN_E_WORKSPACE.
+ */
+int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
+                     int B, int H, int S_q, int S_kv, int D_h,
+                     int causal, float scale, int dtype, void *stream,
+                     int kv_len, int n_split, void *workspace, size_t workspace_bytes);
+
+/* Workspace bytes attn_fwd_splitkv needs (0 for n_split = 1): n_split * B*H*S_q
+ * * 264.  Host only.  ATTN_E_SHAPE for sizes < 1 or an overflow, ATTN_E_SPLIT
+ * for n_split out of range. */
+int attn_splitkv_workspace_bytes(int B, int H, int S_q, int n_split, size_t *bytes);
+
+/* A key-range count for attn_fwd_splitkv on a GPU of n_cu compute units: 1
+ * when there are at least two 128-row query tiles per CU or the keys span
+ * fewer than 16 64-key tiles; otherwise enough ranges for two workgroups per
+ * CU, keeping at least 8 key tiles per range.  Host only.  ATTN_E_SHAPE for
+ * sizes < 1 or a NULL output. */
+int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, int *n_split);
 
 /*
  * attn_kv_append -- write n_new new key and value rows into a K/V cache at

@@ -230,3 +230,63 @@ def test_varlen_valid_call_without_gpu_reports_device():
     assert call_varlen(S_q=200, S_kv=120) == 9
     assert call_varlen(lens=LENS + 4, dtype=0, causal=0) == 9   # 4-byte alignment is enough for the lengths
 
+
+
+# attn_fwd_splitkv: key ranges across workgroups, a caller-owned workspace.
+WS = 0x800000
+GOOD_SPLIT = dict(q=Q, k=K, v=V, o=O, B=2, H=3, S_q=100, S_kv=120, D=64, causal=1, scale=0.125, dtype=2,
+                  kv_len=120, n=4, ws=WS, ws_bytes=4 * 2 * 3 * 100 * 264)
+
+
+def call_split(**kw):
+    a = dict(GOOD_SPLIT, **kw)
+    return A.lib.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["S_q"], a["S_kv"], a["D"],
+                                  a["causal"], a["scale"], a["dtype"], None, a["kv_len"], a["n"], a["ws"],
+                                  a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(B=0), 2), (dict(D=32), 2), (dict(dtype=7), 3), (dict(scale=float("inf")), 4),
+    (dict(S_q=121, kv_len=120), 5), (dict(kv_len=0), 6), (dict(kv_len=121), 6), (dict(k=K + 2), 7),
+    (dict(o=K), 8),
+    (dict(n=0), 11), (dict(n=-3), 11), (dict(n=1025), 11),
+    (dict(ws=0), 12), (dict(ws=WS + 8), 12), (dict(ws_bytes=4 * 2 * 3 * 100 * 264 - 1), 12),
+    (dict(ws=Q), 12), (dict(ws=V - 1024), 12), (dict(ws=O + 16), 12),
+])
+def test_splitkv_invalid_arguments_return_their_code(kw, code):
+    assert call_split(**kw) == code
+
+
+def test_splitkv_valid_calls_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_split() == 9
+    assert call_split(n=1, ws=0, ws_bytes=0) == 9        # one range needs no workspace
+    assert call_split(n=1024, ws_bytes=1024 * 2 * 3 * 100 * 264) == 9
+
+
+def test_splitkv_workspace_bytes():
+    assert A.splitkv_workspace_bytes(2, 3, 100, 1) == 0
+    assert A.splitkv_workspace_bytes(2, 3, 100, 4) == 4 * 2 * 3 * 100 * (64 + 2) * 4
+    assert A.splitkv_workspace_bytes(16, 16, 1, 8) == 8 * 256 * 264
+    with pytest.raises(A.AttnError):
+        A.splitkv_workspace_bytes(2, 3, 100, 0)
+    with pytest.raises(A.AttnError):
+        A.splitkv_workspace_bytes(1 << 20, 1 << 10, 1 << 20, 1024)   # overflows int64
+
+
+@pytest.mark.parametrize("B,H,S_q,kv_len,n_cu,expect", [
+    (32, 16, 1024, 1024, 256, 1),      # 4096 query tiles: no split
+    (4, 8, 2048, 2048, 256, 1),        # 512 tiles = two per CU
+    (16, 16, 1, 98304, 256, 2),        # a decode step of the long cache: 256 tiles -> two ranges
+    (1, 1, 1, 98304, 256, 192),        # one head: 1536 key tiles, at least 8 per range
+    (1, 1, 128, 128, 256, 1),          # two key tiles: too short to split
+    (2, 4, 16, 4096, 256, 8),          # 8 tiles want 64 ranges; 64 key tiles allow 64 // 8 = 8
+    (1, 2, 300, 8192, 256, 16),        # 6 tiles want 86 ranges; 128 key tiles allow 16
+    (4, 8, 1, 2048, 256, 4),           # a decode step of 32 heads: 32 key tiles allow 4
+    (4, 8, 1, 960, 256, 1),            # 15 key tiles: too short to split
+])
+def test_splitkv_choose(B, H, S_q, kv_len, n_cu, expect):
+    got = A.splitkv_choose(B, H, S_q, kv_len, n_cu)
+    assert got == expect

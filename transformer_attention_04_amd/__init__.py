@@ -8,6 +8,7 @@ built, importing this package raises.
     attn_fwd(q, k, v, causal=False, scale=None)            -> o
     attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o
     attn_fwd_varlen(q, k, v, kv_lens, causal=False, ...)     -> o
+    attn_fwd_splitkv(q, k, v, causal=False, n_split=0, ...)  -> o
     attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len)   -> kv_len + n
     attn_strerror(status)                                    -> str
 
@@ -28,9 +29,10 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_DTYPE", 4: "ATTN_E_SCALE",
     5: "ATTN_E_CAUSAL", 6: "ATTN_E_CHUNK", 7: "ATTN_E_ALIGN", 8: "ATTN_E_OVERLAP",
-    9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH",
+    9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH", 11: "ATTN_E_SPLIT", 12: "ATTN_E_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_kv_append", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
+EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
+           "attn_splitkv_choose", "attn_kv_append", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
 
 
 class AttnError(RuntimeError):
@@ -43,6 +45,15 @@ def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run transformer_attention_04_amd/build.py "
                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    # torch ships its own HIP runtime under the same soname as the system one
+    # this library links.  Loaded after torch, the library binds to torch's
+    # copy; loaded first, it would pull in the system runtime and torch would
+    # then load its own as well: two runtimes in one process, and torch's
+    # streams and memory would be foreign to this library's calls.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp]
@@ -51,6 +62,13 @@ def _load(path: str = LIB_PATH):
     lib.attn_fwd_chunked.restype = i
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, vp]
     lib.attn_fwd_varlen.restype = i
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, i, i, vp,
+                                     ctypes.c_size_t]
+    lib.attn_fwd_splitkv.restype = i
+    lib.attn_splitkv_workspace_bytes.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_splitkv_workspace_bytes.restype = i
+    lib.attn_splitkv_choose.argtypes = [i, i, i, i, i, ctypes.POINTER(i)]
+    lib.attn_splitkv_choose.restype = i
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_kv_append.restype = i
     lib.attn_strerror.argtypes = [i]
@@ -173,6 +191,54 @@ def attn_fwd_varlen(q, k, v, kv_lens, causal: bool = False, scale: float | None 
     st = _call(lib.attn_fwd_varlen, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                B, H, S_q, S_kv, D, int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(dev, stream),
                kv_lens.data_ptr())
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return o
+
+
+def splitkv_workspace_bytes(B: int, H: int, S_q: int, n_split: int) -> int:
+    n = ctypes.c_size_t()
+    st = lib.attn_splitkv_workspace_bytes(B, H, S_q, n_split, ctypes.byref(n))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return n.value
+
+
+def splitkv_choose(B: int, H: int, S_q: int, kv_len: int, n_cu: int) -> int:
+    n = ctypes.c_int()
+    st = lib.attn_splitkv_choose(B, H, S_q, kv_len, n_cu, ctypes.byref(n))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return n.value
+
+
+def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, kv_len: int | None = None,
+                     n_split: int = 0, out=None, workspace=None, stream=None):
+    """One query window against the first kv_len K/V rows with the keys split
+    over n_split workgroup ranges and merged (see attn_fwd_splitkv in
+    include/attn.h).  n_split=0 asks attn_splitkv_choose for this GPU's CU
+    count.  workspace: a uint8 GPU tensor of at least splitkv_workspace_bytes
+    bytes (allocated here when None)."""
+    torch = _t()
+    B, H, S_q, S_kv, D = _check(q, k, v)
+    if kv_len is None:
+        kv_len = S_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if n_split == 0:
+        n_split = splitkv_choose(B, H, S_q, kv_len, torch.cuda.get_device_properties(dev).multi_processor_count)
+    need = splitkv_workspace_bytes(B, H, S_q, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    st = _call(lib.attn_fwd_splitkv, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+               B, H, S_q, S_kv, D, int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(dev, stream),
+               int(kv_len), int(n_split), workspace.data_ptr(), workspace.numel() * workspace.element_size())
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o

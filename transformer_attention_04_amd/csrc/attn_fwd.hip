@@ -67,6 +67,8 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int HEAD_DIM = 64;
 constexpr int BM = 128;        // query rows per workgroup
 constexpr int BN = 64;         // keys per iteration
+constexpr int MAX_SPLIT = 1024;          // key ranges per call, at most
+constexpr int SPLIT_MIN_KV_TILES = 16;   // the automatic split leaves shorter key chains whole
 constexpr int NTHREADS = 256;  // 4 wavefronts of 64
 constexpr float LAZY_TH = 8.0f;       // log2 headroom before the offset is raised
 constexpr float P_LIMIT = 32768.0f;  // largest per-lane block sum taken without a max
@@ -150,6 +152,15 @@ struct Params {
   const int* kv_lens;  // per-sequence valid K/V rows (device, B values) or null: kv_len for all
   int H;
   int S_kv;
+  // Key split across workgroups (ws_acc null: none).  Split s covers keys
+  // [s * split_span, (s + 1) * split_span); its workgroups are blocks
+  // s * base_grid .. +base_grid-1, and write the unnormalised partial state of
+  // each row (index (s * bh + head) * S_q + row) for the merge kernel.
+  float* ws_acc;   // [n_split][bh * S_q][64] fp32 acc
+  float* ws_ml;    // [n_split][bh * S_q][2] fp32 (offset m, row sum l)
+  int split_span;  // keys per split
+  int base_grid;   // workgroups per split
+  int bh;          // B * H
 };
 
 __device__ __forceinline__ float other_half(float x) {
@@ -564,7 +575,10 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 //
 // VARLEN: each sequence has its own key length, read from p.kv_lens (key
 // padding); a row that then sees no key gets zeros.
-template <typename T, bool CAUSAL, int KS, bool VARLEN>
+// SPLIT: the workgroup covers one key range of its query rows (the cache is
+// viewed from the range's first row on, with the causal shift of the whole
+// cache) and writes the partial (m, l, acc) instead of O.
+template <typename T, bool CAUSAL, int KS, bool VARLEN, bool SPLIT>
 __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2 : 1)
     attn_fwd_kernel(Params<T> p) {
   constexpr bool F32 = sizeof(T) == 4;
@@ -581,7 +595,12 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   __shared__ __attribute__((aligned(16))) char st2[NS == 3 ? STAGE : 16];
 
   int head, row0, row1;
-  decode_tile(p.s, blockIdx.x, head, row0, row1);
+  int split = 0, tile_id = blockIdx.x;
+  if constexpr (SPLIT) {
+    split = tile_id / p.base_grid;
+    tile_id -= split * p.base_grid;
+  }
+  decode_tile(p.s, tile_id, head, row0, row1);
 
   const int tid = threadIdx.x;
   // 0 .. 4*KS-1.  Deliberately not made compiler-uniform (readfirstlane):
@@ -596,16 +615,20 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   const int hf = lane >> 5;   // half-wave
 
   const T* qh = p.q + (int64_t)head * p.q_head_stride;
-  const T* kh_ptr = p.k + (int64_t)head * p.kv_head_stride;
-  const T* vh_ptr = p.v + (int64_t)head * p.kv_head_stride;
+  const int k_start = SPLIT ? split * p.split_span : 0;  // first key of this workgroup's range
+  const T* kh_ptr = p.k + (int64_t)head * p.kv_head_stride + (int64_t)k_start * HEAD_DIM;
+  const T* vh_ptr = p.v + (int64_t)head * p.kv_head_stride + (int64_t)k_start * HEAD_DIM;
   T* oh = p.o + (int64_t)head * p.q_head_stride;
 
   // Valid K/V rows of this head's sequence: kv_len, or its own length
   // clamped into the cache (a row that sees no key gets zeros).
-  const int kv_len = VARLEN ? min(max(p.kv_lens[head / p.H], 0), p.S_kv) : p.kv_len;
-  const int shift = kv_len - p.S_q;  // absolute position of query row r is r + shift
+  const int kv_full = VARLEN ? min(max(p.kv_lens[head / p.H], 0), p.S_kv) : p.kv_len;
+  // From here on keys are counted from k_start: the range holds kv_len of
+  // them, and query row r sits at position r + shift.
+  const int kv_len = SPLIT ? max(0, min(kv_full, k_start + p.split_span) - k_start) : kv_full;
+  const int shift = kv_full - p.S_q - k_start;
   const int kv_end0 = CAUSAL ? min(kv_len, row1 + shift) : kv_len;
-  const int kv_end = VARLEN ? max(0, kv_end0) : kv_end0;
+  const int kv_end = (VARLEN || SPLIT) ? max(0, kv_end0) : kv_end0;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const int n_super = (n_tiles + KS - 1) / KS;
 
@@ -924,6 +947,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
     const float a0 = (m == -INFINITY) ? 0.f : fast_exp2(m - mt);
     const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mt);
     l = l * a0 + l1 * a1;
+    if constexpr (SPLIT) m = mt;  // the merged state's offset
 #pragma unroll
     for (int qd = 0; qd < 8; ++qd) {
       const u32x4 w = racc[(qg * 8 + qd) * 64 + lane];
@@ -943,6 +967,41 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
   // targets it any more); with the key split, the wave's own part of the
   // merge area, which it has read.
   const float lt = l + other_half(l);
+  if constexpr (SPLIT) {
+    // This key range's state of each valid row, one row per lane: fp32 acc
+    // (its half of the columns per half-wave), and (m, l) from half-wave 0.
+    if (qrow < row1) {
+      const int64_t prow = ((int64_t)split * p.bh + head) * p.S_q + qrow;
+      float* wa = p.ws_acc + prow * HEAD_DIM;
+      if constexpr (F32) {
+        // acc[dt] register 4g + e is column 16g + 8hf + 2e + dt
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const u32x4 w0 = {__float_as_uint(acc[0][4 * gq]), __float_as_uint(acc[1][4 * gq]),
+                            __float_as_uint(acc[0][4 * gq + 1]), __float_as_uint(acc[1][4 * gq + 1])};
+          const u32x4 w1 = {__float_as_uint(acc[0][4 * gq + 2]), __float_as_uint(acc[1][4 * gq + 2]),
+                            __float_as_uint(acc[0][4 * gq + 3]), __float_as_uint(acc[1][4 * gq + 3])};
+          *reinterpret_cast<u32x4*>(wa + 16 * gq + 8 * hf) = w0;
+          *reinterpret_cast<u32x4*>(wa + 16 * gq + 8 * hf + 4) = w1;
+        }
+      } else {
+        // acc[dt] register 4g + e is column 32dt + 8g + 4hf + e
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const u32x4 w = {__float_as_uint(acc[dt][4 * gq]), __float_as_uint(acc[dt][4 * gq + 1]),
+                             __float_as_uint(acc[dt][4 * gq + 2]), __float_as_uint(acc[dt][4 * gq + 3])};
+            *reinterpret_cast<u32x4*>(wa + 32 * dt + 8 * gq + 4 * hf) = w;
+          }
+      }
+      if (hf == 0) {
+        const u32x2 ml = {__float_as_uint(m), __float_as_uint(lt)};
+        *reinterpret_cast<u32x2*>(p.ws_ml + 2 * prow) = ml;
+      }
+    }
+    return;
+  }
   const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
   // An opaque lane index: the store rows below equal the Q copy rows of the
   // prologue, which the compiler would otherwise keep live across the loop.
@@ -999,6 +1058,45 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 128 + 16 * (ch ^ (row & 7)));
       if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 8 * ch) = x;
     }
+  }
+}
+
+// Merge of the key ranges: row r's ranges hold (m_s, l_s, acc_s) with
+// acc_s and l_s relative to 2^m_s; with M = max m_s the row is
+// O = sum 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s (a range in which the row
+// saw no key has m_s = -inf and weight 0; a row that saw none at all gets
+// zeros).  One thread per row and 16-byte chunk of its 64 columns.
+constexpr int MERGE_THREADS = 256;
+
+template <typename T>
+__global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const float* __restrict__ ws_acc,
+                                                                      const float* __restrict__ ws_ml,
+                                                                      T* __restrict__ o, int64_t rows, int n_split) {
+  const int64_t t = (int64_t)blockIdx.x * MERGE_THREADS + threadIdx.x;
+  if (t >= rows * 16) return;
+  const int64_t row = t >> 4;
+  const int ch = (int)(t & 15);
+  float mx = -INFINITY;
+  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, ws_ml[2 * (s * rows + row)]);
+  float L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < n_split; ++s) {
+    const int64_t pr = s * rows + row;
+    const float m = ws_ml[2 * pr];
+    if (m == -INFINITY) continue;
+    const float w = fast_exp2(m - mx);
+    L += w * ws_ml[2 * pr + 1];
+    const u32x4 x = *reinterpret_cast<const u32x4*>(ws_acc + pr * HEAD_DIM + 4 * ch);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += w * __uint_as_float(x[e]);
+  }
+  const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+  if constexpr (sizeof(T) == 4) {
+    const u32x4 w = {__float_as_uint(a[0] * inv), __float_as_uint(a[1] * inv), __float_as_uint(a[2] * inv),
+                     __float_as_uint(a[3] * inv)};
+    *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(o) + row * HEAD_DIM + 4 * ch) = w;
+  } else {
+    const u32x2 w = {Half16<T>::pack2(a[0] * inv, a[1] * inv), Half16<T>::pack2(a[2] * inv, a[3] * inv)};
+    *reinterpret_cast<u32x2*>(o + row * HEAD_DIM + 4 * ch) = w;
   }
 }
 
@@ -1077,26 +1175,28 @@ Sched make_sched(int B, int H, int S_q, int chunk, int kv_len, int causal) {
   return s;
 }
 
-template <typename T, int KS, bool VARLEN>
+template <typename T, int KS, bool VARLEN, bool SPLIT>
 void launch_kernel_v(const Params<T>& p, int grid, int causal, hipStream_t stream) {
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS, VARLEN>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS, VARLEN, SPLIT>), dim3(grid), dim3(NTHREADS * KS), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS, VARLEN>), dim3(grid), dim3(NTHREADS * KS), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS, VARLEN, SPLIT>), dim3(grid), dim3(NTHREADS * KS), 0, stream,
+                       p);
 }
 
 template <typename T, int KS>
 void launch_kernel(const Params<T>& p, int grid, int causal, hipStream_t stream) {
   if (p.kv_lens)
-    launch_kernel_v<T, KS, true>(p, grid, causal, stream);
+    launch_kernel_v<T, KS, true, false>(p, grid, causal, stream);
   else
-    launch_kernel_v<T, KS, false>(p, grid, causal, stream);
+    launch_kernel_v<T, KS, false, false>(p, grid, causal, stream);
 }
 
 template <typename T>
 int launch_typed(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
                  int causal, float scale, hipStream_t stream, int chunk, int kv_len, int n_cu,
-                 const int* kv_lens = nullptr) {
+                 const int* kv_lens = nullptr, int n_split = 1, void* ws = nullptr) {
   Params<T> p;
   p.q = static_cast<const T*>(q);
   p.k = static_cast<const T*>(k);
@@ -1109,6 +1209,10 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   p.kv_lens = kv_lens;
   p.H = H;
   p.S_kv = S_kv;
+  p.ws_acc = nullptr;
+  p.ws_ml = nullptr;
+  p.split_span = 0;
+  p.bh = B * H;
   // |scale| * log2(e), at least 1e-30 so that a masked score (-inf) always
   // exponentiates to 0; for scale = 0 every visible probability is still
   // exp2(~1e-27) = 1 exactly in fp32.
@@ -1116,6 +1220,29 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   p.q_flip = (scale < 0.f) ? (sizeof(T) == 4 ? 0x80000000u : 0x80008000u) : 0u;
   p.s = make_sched(B, H, S_q, chunk, kv_len, causal);
   const int grid = p.s.groups * p.s.heads * (p.s.tl + (p.s.n_win - 1) * p.s.tf);
+  p.base_grid = grid;
+  if (n_split > 1) {
+    // Split the keys into n_split ranges of whole 64-key tiles; the four-wave
+    // workgroup runs every range (two per CU keep more tile copies in flight
+    // than one eight-wave workgroup).  Ranges past the last tile are empty.
+    const int kv_tiles = (kv_len + BN - 1) / BN;
+    const int per = (kv_tiles + n_split - 1) / n_split;
+    p.split_span = per * BN;
+    p.ws_acc = static_cast<float*>(ws);
+    const int64_t rows = (int64_t)B * H * S_q;
+    p.ws_ml = p.ws_acc + (int64_t)n_split * rows * HEAD_DIM;
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, true, 1, false, true>), dim3(grid * n_split), dim3(NTHREADS), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<T, false, 1, false, true>), dim3(grid * n_split), dim3(NTHREADS), 0,
+                         stream, p);
+    if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+    const int64_t mblocks = (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS;
+    hipLaunchKernelGGL((splitkv_merge_kernel<T>), dim3((unsigned)mblocks), dim3(MERGE_THREADS), 0, stream,
+                       p.ws_acc, p.ws_ml, static_cast<T*>(o), rows, n_split);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  }
   // Few 128-row query tiles (at most two per CU): split each tile's key range
   // between two wave groups so every SIMD runs two waves on half the key
   // chain.  The choice depends on B, H and S_q only, never on the window
@@ -1237,6 +1364,71 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   }
 }
 
+extern "C" int attn_splitkv_workspace_bytes(int B, int H, int S_q, int n_split, size_t* bytes) {
+  if (!bytes || B < 1 || H < 1 || S_q < 1) return ATTN_E_SHAPE;
+  if (n_split < 1 || n_split > MAX_SPLIT) return ATTN_E_SPLIT;
+  if (n_split == 1) {
+    *bytes = 0;
+    return ATTN_OK;
+  }
+  const int64_t rows = (int64_t)B * H * S_q;
+  const int64_t per_row = (HEAD_DIM + 2) * 4;  // fp32 acc, then (m, l)
+  if (rows > INT64_MAX / per_row / n_split) return ATTN_E_SHAPE;
+  *bytes = (size_t)(rows * per_row * n_split);
+  return ATTN_OK;
+}
+
+extern "C" int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, int* n_split) {
+  if (!n_split || B < 1 || H < 1 || S_q < 1 || kv_len < 1 || n_cu < 1) return ATTN_E_SHAPE;
+  const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
+  const int64_t kv_tiles = (kv_len + BN - 1) / BN;
+  int64_t n = 1;
+  if (tiles < 2 * (int64_t)n_cu && kv_tiles >= SPLIT_MIN_KV_TILES) {
+    n = (2 * (int64_t)n_cu + tiles - 1) / tiles;                 // at least two workgroups per CU
+    n = std::min<int64_t>(n, kv_tiles / (SPLIT_MIN_KV_TILES / 2));  // each range keeps a long key chain
+    n = std::max<int64_t>(1, std::min<int64_t>(n, MAX_SPLIT));
+  }
+  *n_split = (int)n;
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
+                                int S_kv, int D_h, int causal, float scale, int dtype, void* stream, int kv_len,
+                                int n_split, void* workspace, size_t workspace_bytes) {
+  const int st = validate(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, S_q, kv_len);
+  if (st != ATTN_OK) return st;
+  size_t need = 0;
+  const int ws = attn_splitkv_workspace_bytes(B, H, S_q, n_split, &need);
+  if (ws != ATTN_OK) return ws;
+  const Sched sc = make_sched(B, H, S_q, S_q, kv_len, causal);
+  const int64_t grid = (int64_t)sc.groups * sc.heads * sc.tl;
+  const int64_t rows = (int64_t)B * H * S_q;
+  if (grid * n_split > INT32_MAX || (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS > INT32_MAX) return ATTN_E_SPLIT;
+  if (n_split > 1) {
+    if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return ATTN_E_WORKSPACE;
+    const uint64_t esz = dtype == ATTN_F32 ? 4 : 2;
+    const uint64_t nq = (uint64_t)rows * HEAD_DIM * esz, nkv = (uint64_t)B * H * S_kv * HEAD_DIM * esz;
+    if (ranges_overlap(workspace, need, q, nq) || ranges_overlap(workspace, need, o, nq) ||
+        ranges_overlap(workspace, need, k, nkv) || ranges_overlap(workspace, need, v, nkv))
+      return ATTN_E_WORKSPACE;
+  }
+  int n_cu = 0;
+  const int dv = check_device(&n_cu);
+  if (dv != ATTN_OK) return dv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case ATTN_F32:
+      return launch_typed<float>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, kv_len, n_cu, nullptr, n_split,
+                                 workspace);
+    case ATTN_F16:
+      return launch_typed<_Float16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, kv_len, n_cu, nullptr,
+                                    n_split, workspace);
+    default:
+      return launch_typed<__bf16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, kv_len, n_cu, nullptr,
+                                  n_split, workspace);
+  }
+}
+
 extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int* grid) {
   if (B < 1 || H < 1 || S_q < 1 || chunk < 1 || kv_len < 1 || !grid) return ATTN_E_SHAPE;
   const int64_t bh = (int64_t)B * H;
@@ -1271,6 +1463,8 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_E_OVERLAP: return "output overlaps an input";
     case ATTN_E_DEVICE: return "current HIP device missing or not gfx950";
     case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_SPLIT: return "n_split outside [1, 1024], or the split grid is too large";
+    case ATTN_E_WORKSPACE: return "workspace null, not 16-byte aligned, too small, or overlapping a tensor";
     default: return "unknown attn status";
   }
 }
