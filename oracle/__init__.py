@@ -15,6 +15,8 @@ padded to one K/V capacity: per sequence, the same function on its own K/V
 prefix (a slice), with the bottom-right causal rule of that sequence's length
 and zeros for a query row that sees no key.  ``kv_append`` is the K/V cache
 append of the streaming use, a numpy slice assignment (no arithmetic).
+``qkv_projection`` is the fused Q/K/V projection upstream of attention: one
+matrix product with the stacked weights, in fp64, split into heads.
 
 Parity status of each function is stated where it is tested (``tests/
 test_oracle_pins.py``): the attention function is pinned by closed forms,
@@ -22,7 +24,9 @@ invariants, a library special case (torch CPU float64 SDPA with an explicit
 mask) and 50-digit brute force; ``attention_varlen`` by SDPA with a
 per-sequence mask, padding that holds NaN, empty and single-key rows and
 batch permutations; ``kv_append`` by an element-by-element loop, two appends
-against one, and raw bit patterns; none is "parity unpinned".
+against one, and raw bit patterns; ``qkv_projection`` by brute-force loops,
+identity and zero-input closed forms, head permutations and linearity; none is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -150,6 +154,27 @@ def attention_varlen(q, k, v, kv_lens, *, causal: bool = False, scale: float | N
         o[b:b + 1, :, i0:] = attention(q[b:b + 1, :, i0:], k[b:b + 1, :, :L], v[b:b + 1, :, :L],
                                        causal=causal, scale=scale, threads=threads, lib=lib)
     return o
+
+
+def qkv_projection(x, w, bias, H: int):
+    """The fused Q/K/V projection (page "Roofline", sections "What it does" and
+    "How we built it": the three projections of a layer's input as one larger
+    kernel).  x: [B, S, d] with d = 64*H; w: [3d, d], the three projection
+    weights stacked in the layout of a linear layer (output feature o is row
+    o; rows [0, d) give Q, [d, 2d) K, [2d, 3d) V; inside each, head h is
+    features [64h, 64h + 64)); bias: [3d] or None.  y = x w^T + bias in fp64;
+    returns (q, k, v), each float64 [B, H, S, 64] with q[b, h, s, e] =
+    y[b, s, 64h + e] and likewise k, v from the next two thirds."""
+    x = np.asarray(_f32(x), dtype=np.float64)
+    w = np.asarray(_f32(w), dtype=np.float64)
+    B, S, d = x.shape
+    if d != 64 * H or w.shape != (3 * d, d):
+        raise ValueError(f"shapes x{x.shape} w{w.shape} do not match H={H}, head size 64")
+    y = x.reshape(B * S, d) @ w.T
+    if bias is not None:
+        y = y + np.asarray(_f32(bias), dtype=np.float64).reshape(1, 3 * d)
+    y = y.reshape(B, S, 3, H, 64)
+    return tuple(np.ascontiguousarray(y[:, :, j].transpose(0, 2, 1, 3)) for j in range(3))
 
 
 def kv_append(k_cache, v_cache, k_new, v_new, kv_len):

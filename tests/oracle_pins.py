@@ -453,3 +453,85 @@ VARLEN_CHECKS = [
     check_varlen_sdpa, check_varlen_padding_ignored, check_varlen_empty_and_single_key_rows,
     check_varlen_full_lengths_equal_attention, check_varlen_batch_permutation,
 ]
+
+
+# --------------------------------------------------------------------------
+# fused Q/K/V projection: checks take ``proj``, a callable with the signature
+# of ``oracle.qkv_projection``
+# --------------------------------------------------------------------------
+def check_proj_bruteforce(proj):
+    # explicit loops over every output element, with the stacking and head
+    # split written out index by index
+    r = _rng(700)
+    for B, S, H, with_bias in ((1, 3, 1, True), (2, 2, 2, False), (2, 5, 1, True)):
+        d = 64 * H
+        x = _randn(r, (B, S, d))
+        w = _randn(r, (3 * d, d))
+        bias = _randn(r, (3 * d,)) if with_bias else None
+        q, k, v = proj(x, w, bias, H)
+        outs = (q, k, v)
+        for j in range(3):
+            for b in range(B):
+                for h in range(H):
+                    for s in range(S):
+                        for e in range(64):
+                            o = j * d + h * 64 + e
+                            ref = math.fsum(float(x[b, s, i]) * float(w[o, i]) for i in range(d))
+                            if bias is not None:
+                                ref += float(bias[o])
+                            assert abs(outs[j][b, h, s, e] - ref) <= 1e-9 * (1 + abs(ref)), (j, b, h, s, e)
+
+
+def check_proj_identity_weights(proj):
+    # W = [I; 2I; -I]: Q is the input split into heads, K twice it, V minus it
+    B, S, H = 2, 7, 3
+    d = 64 * H
+    x = _randn(_rng(701), (B, S, d))
+    eye = np.eye(d, dtype=np.float32)
+    q, k, v = proj(x, np.concatenate([eye, 2 * eye, -eye]), None, H)
+    heads = x.reshape(B, S, H, 64).transpose(0, 2, 1, 3).astype(np.float64)
+    assert np.array_equal(q, heads) and np.array_equal(k, 2 * heads) and np.array_equal(v, -heads)
+
+
+def check_proj_zero_input_gives_bias(proj):
+    B, S, H = 1, 4, 2
+    d = 64 * H
+    bias = _randn(_rng(702), (3 * d,))
+    q, k, v = proj(np.zeros((B, S, d), np.float32), _randn(_rng(703), (3 * d, d)), bias, H)
+    for j, t in enumerate((q, k, v)):
+        for h in range(H):
+            assert np.all(t[:, h] == bias[j * d + 64 * h: j * d + 64 * h + 64].astype(np.float64))
+
+
+def check_proj_head_permutation(proj):
+    # permuting the heads' row blocks of each third of W permutes the output heads
+    B, S, H = 2, 3, 4
+    d = 64 * H
+    r = _rng(704)
+    x, w = _randn(r, (B, S, d)), _randn(r, (3 * d, d))
+    perm = np.array([2, 0, 3, 1])
+    rows = np.concatenate([j * d + 64 * p + np.arange(64) for j in range(3) for p in perm])
+    a = proj(x, w, None, H)
+    c = proj(x, w[rows], None, H)
+    for j in range(3):
+        assert np.array_equal(c[j], a[j][:, perm])
+
+
+def check_proj_linearity(proj):
+    B, S, H = 2, 3, 1
+    d = 64 * H
+    r = _rng(705)
+    # inputs on a 2^-6 grid so that 0.5 x1 + 2 x2 is exact in fp32
+    x1, x2 = _randn(r, (B, S, d), step=2.0 ** -6), _randn(r, (B, S, d), step=2.0 ** -6)
+    w, bias = _randn(r, (3 * d, d)), _randn(r, (3 * d,))
+    f = lambda x: proj(x, w, bias, H)
+    a, b2, c = f(x1), f(x2), f((0.5 * x1 + 2.0 * x2).astype(np.float32))
+    z = f(np.zeros_like(x1))
+    for j in range(3):
+        lhs = c[j] - z[j]
+        rhs = 0.5 * (a[j] - z[j]) + 2.0 * (b2[j] - z[j])
+        assert np.max(np.abs(lhs - rhs)) <= 1e-9
+
+
+PROJ_CHECKS = [check_proj_bruteforce, check_proj_identity_weights, check_proj_zero_input_gives_bias,
+               check_proj_head_permutation, check_proj_linearity]

@@ -97,3 +97,33 @@ def test_varlen_mutant_is_caught(name, old, new):
             caught.append(check.__name__)
             break
     assert caught, f"varlen mutant {name} passed every pin"
+
+
+# The Q/K/V projection (numpy in oracle/__init__.py): one planted slip per
+# mutant in a copy of its source text.
+PROJ_MUTANTS = [
+    ("weights_not_transposed", "y = x.reshape(B * S, d) @ w.T", "y = x.reshape(B * S, d) @ w[:d].T.repeat(3, 1).T.T"),
+    ("bias_dropped", "y = y + np.asarray(_f32(bias), dtype=np.float64).reshape(1, 3 * d)", "y = y"),
+    ("heads_before_thirds", "y = y.reshape(B, S, 3, H, 64)", "y = y.reshape(B, S, H, 3, 64).transpose(0, 1, 3, 2, 4)"),
+    ("k_and_v_swapped", "for j in range(3))", "for j in (0, 2, 1))"),
+    ("sequence_and_head_axes_kept", "y[:, :, j].transpose(0, 2, 1, 3)", "y[:, :, j].reshape(B, H, S, 64)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PROJ_MUTANTS, ids=[m[0] for m in PROJ_MUTANTS])
+def test_projection_mutant_is_caught(name, old, new):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(oracle.qkv_projection))
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), ns)
+    mutant = ns["qkv_projection"]
+    caught = []
+    for check in pins.PROJ_CHECKS:
+        try:
+            check(mutant)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"projection mutant {name} passed every pin"

@@ -23,6 +23,11 @@ def test_varlen_pin(check):
     check(oracle.attention_varlen)
 
 
+@pytest.mark.parametrize("check", pins.PROJ_CHECKS, ids=lambda f: f.__name__)
+def test_projection_pin(check):
+    check(oracle.qkv_projection)
+
+
 def _heads(x, n):
     return x[:1, :n].contiguous()
 
