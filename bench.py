@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--decode", type=int, default=None, metavar="R",
                     help="R query rows (the last R positions) against the workload's whole K/V cache through "
                          "attn_fwd_splitkv (keys split over workgroup ranges and merged)")
+    ap.add_argument("--qkv", action="store_true",
+                    help="the fused Q/K/V projection (attn_qkv_proj) of a [B, S, 64H] input with synthetic "
+                         "weights [3d, d] and bias; value is its TFLOP/s (2 * B*S * 3d * d per call)")
     ap.add_argument("--n-split", type=int, default=0,
                     help="key ranges for --decode (0: attn_splitkv_choose for this GPU)")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
@@ -129,14 +132,17 @@ def roofline_for(w, dtype, sec_per_call, work=None):
             "frac": round(ach / pk, 4), "traffic": None}
 
 
-def code_key(path):
-    """sha256 prefix of a C++/HIP source with its comments removed and its
-    whitespace collapsed: it changes when the code changes, not when a comment
-    does.  (The kernel source holds no string literal with a comment marker.)"""
+def code_key(paths):
+    """sha256 prefix of C++/HIP sources (one path or a list, concatenated)
+    with comments removed and whitespace collapsed: it changes when the code
+    changes, not when a comment does.  (The kernel sources hold no string
+    literal with a comment marker.)"""
     import hashlib
     import re
-    with open(path) as f:
-        src = f.read()
+    src = ""
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path) as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
@@ -149,7 +155,8 @@ def measured_traffic(workload, dtype):
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             t = json.load(f)
-        key = code_key(os.path.join(ROOT, t["kernel_source"]))
+        srcs = t["kernel_source"]
+        key = code_key([os.path.join(ROOT, x) for x in ([srcs] if isinstance(srcs, str) else srcs)])
     except (OSError, KeyError, ValueError):
         return None
     e = t.get("entries", {}).get(f"{workload}/{dtype}")
@@ -255,6 +262,98 @@ def split_steps(k, r):
     return [k // r + (1 if i < k % r else 0) for i in range(r)]
 
 
+def bench_qkv(args, w, dtype):
+    """Time attn_qkv_proj on the workload's batch, sequence and heads."""
+    import torch
+    import workloads as W
+    import transformer_attention_04_amd as A
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, S, H = w.B, w.S_q, w.H
+    d = 64 * H
+    t = W.DTYPES[dtype]
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 700)
+    wt = (torch.randn((3 * d, d), generator=g, device=dev) / d ** 0.5).to(t)
+    bias = (torch.randn((3 * d,), generator=g, device=dev) * 0.1).to(t)
+    x0 = torch.randn((B, S, d), generator=g, device=dev).to(t)
+    per_set = 4 * B * S * d * 2
+    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
+    sets = [(x0 if i == 0 else x0.clone(), tuple(torch.empty((B, H, S, 64), dtype=t, device=dev) for _ in range(3)))
+            for i in range(n_sets)]
+    flops = 2.0 * B * S * 3 * d * d
+    nbytes = (B * S * d + 3 * d * d + 3 * d + 3 * B * S * d) * 2
+    log(f"[bench] qkv projection B={B} S={S} d={d} {dtype}: {flops / 1e9:.1f} GFLOP per call, {n_sets} sets")
+
+    def step(i):
+        x, outs = sets[i % n_sets]
+        A.attn_qkv_proj(x, wt, bias, out=outs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    if args.steps is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(10):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        args.steps = int(min(20000, max(10, math.ceil(500.0 / max(e0.elapsed_time(e1) / 10, 1e-3)))))
+    sizes = split_steps(args.steps, args.repeats)
+    graphs = {}
+    if not args.eager:
+        for n in sorted(set(sizes)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(n):
+                    step(i)
+            gr.replay()
+            graphs[n] = gr
+        torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
+    clk0 = gpu_clock_mhz(dev)
+    ev[0].record(stream)
+    for r, n in enumerate(sizes):
+        if graphs:
+            graphs[n].replay()
+        else:
+            for i in range(n):
+                step(i)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    clk1 = gpu_clock_mhz(dev)
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    rep_ms = [ev[r].elapsed_time(ev[r + 1]) / n for r, n in enumerate(sizes)]
+    sec = ms / 1e3
+    tflops = flops / sec / 1e12
+    pk = PEAK[f"mfma_{dtype}"]
+    log(f"[bench] qkv projection {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOP/s ({100 * tflops / pk:.1f}% of peak)")
+    line = {
+        "metric": "fused Q/K/V projection TFLOP/s + % of MFMA peak (ms/call) at 1 GPU", "value": round(tflops, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}_qkv_projection", "B": B, "S": S, "H": H, "d": d, "bias": True,
+                   "rotating_sets": n_sets, "mode": "attn_qkv_proj: x [B,S,d] @ W^T [d,3d] + b -> q,k,v [B,H,S,64]",
+                   "launch": "hip_graph_replay" if graphs else "eager"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": pk, "unit": "TFLOP/s",
+                     "frac": round(tflops / pk, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes},
+        "timing": {"repeats": len(rep_ms), "steps_per_repeat": sizes,
+                   "ms_per_step_each_repeat": [round(x, 6) for x in rep_ms],
+                   "median_ms_per_step": round(sorted(rep_ms)[len(rep_ms) // 2], 6),
+                   "gpu_clock_mhz": {"before": clk0, "after": clk1}},
+        "environment": environment(dev),
+        "cpu_baseline": None,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -270,6 +369,11 @@ def main():
 
     w = W.BY_NAME[args.workload]
     dtype = args.dtype or w.dtypes[0]
+    if args.qkv:
+        if args.varlen or args.stream or args.decode or dtype == "f32":
+            print("--qkv takes a 16-bit dtype and neither --varlen, --stream nor --decode", file=sys.stderr)
+            sys.exit(2)
+        return bench_qkv(args, w, dtype)
     if args.decode:
         if args.varlen or args.stream:
             print("--decode takes neither --varlen nor --stream", file=sys.stderr)

@@ -192,6 +192,33 @@ int attn_splitkv_workspace_bytes(int B, int H, int S_q, int n_split, size_t *byt
 int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, int *n_split);
 
 /*
+ * attn_qkv_proj -- the fused Q/K/V projection upstream of attention (page
+ * "Roofline", sections "What it does" and "How we built it": the three
+ * projections as one larger kernel): y = x W^T (+ bias) as ONE matrix product
+ * whose epilogue writes each head's 64 columns straight into q, k, v in the
+ * [B, H, S, 64] layout the attention entry points read.
+ *   x     : device [B, S, d] (d = 64*H, row-major).
+ *   w     : device [3d, d], the three projection weights stacked in the layout
+ *           of a linear layer: output feature o is row o; rows [0, d) give q,
+ *           [d, 2d) k, [2d, 3d) v, and inside each, head h is rows
+ *           [64h, 64h + 64).
+ *   bias  : device [3d] or NULL (no bias).
+ *   q, k, v : device [B, H, S, 64] outputs: q[b, h, s, e] = y[b*S + s, 64h + e],
+ *           k and v from the next two thirds of y.
+ *   D_h must be 64.  dtype: ATTN_BF16 or ATTN_F16 (all six tensors); fp32
+ *   products accumulate in fp32 (MFMA), the bias is added in fp32, and each
+ *   output is rounded once (RNE) to dtype.
+ * Conventions as above (16-byte aligned base pointers, asynchronous on
+ * `stream`, nothing allocated).  Errors: ATTN_E_NULL (x, w, q, k or v NULL);
+ * ATTN_E_SHAPE (B, S or H < 1, D_h != 64, sizes overflow); ATTN_E_DTYPE
+ * (ATTN_F32 or unknown); ATTN_E_ALIGN; ATTN_E_OVERLAP (an output overlaps an
+ * input or another output); ATTN_E_DEVICE; ATTN_E_LAUNCH.
+ */
+int attn_qkv_proj(const void *x, const void *w, const void *bias,
+                  void *q, void *k, void *v,
+                  int B, int S, int H, int D_h, int dtype, void *stream);
+
+/*
  * attn_kv_append -- write n_new new key and value rows into a K/V cache at
  * row kv_len of every (b, h): the append step of a stream of bounded query
  * windows against a growing key/value cache (page "Roofline", section "How

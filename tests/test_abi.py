@@ -290,3 +290,35 @@ def test_splitkv_workspace_bytes():
 def test_splitkv_choose(B, H, S_q, kv_len, n_cu, expect):
     got = A.splitkv_choose(B, H, S_q, kv_len, n_cu)
     assert got == expect
+
+
+# attn_qkv_proj: x [B, S, 64H], w [3d, d], bias [3d] or NULL, q/k/v [B, H, S, 64].
+PX, PW, PB, PQ, PK_, PV = 0x1000000, 0x2000000, 0x3000000, 0x4000000, 0x5000000, 0x6000000
+GOOD_PROJ = dict(x=PX, w=PW, b=PB, q=PQ, k=PK_, v=PV, B=2, S=100, H=4, D=64, dtype=2)
+
+
+def call_proj(**kw):
+    a = dict(GOOD_PROJ, **kw)
+    return A.lib.attn_qkv_proj(a["x"], a["w"], a["b"], a["q"], a["k"], a["v"], a["B"], a["S"], a["H"], a["D"],
+                               a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), 1), (dict(w=0), 1), (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1),
+    (dict(B=0), 2), (dict(S=0), 2), (dict(H=0), 2), (dict(D=128), 2),
+    (dict(B=1 << 16, S=1 << 16), 2),                  # B*S over 2^31
+    (dict(H=1 << 26), 2),                             # 3d over 2^31
+    (dict(dtype=0), 3), (dict(dtype=9), 3),
+    (dict(x=PX + 8), 7), (dict(b=PB + 2), 7), (dict(v=PV + 4), 7),
+    (dict(q=PX), 8), (dict(k=PW + 64), 8), (dict(v=PB), 8), (dict(k=PQ + 1024), 8),
+])
+def test_proj_invalid_arguments_return_their_code(kw, code):
+    assert call_proj(**kw) == code
+
+
+def test_proj_valid_calls_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_proj() == 9
+    assert call_proj(b=0, dtype=1) == 9      # no bias, fp16

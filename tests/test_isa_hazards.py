@@ -22,15 +22,26 @@ import pytest
 from transformer_attention_04_amd import build as B
 
 
+_ASM = {}
+
+
 def _device_asm(tmp_path):
+    """Device assembly of every kernel source of the library, concatenated
+    (compiled once per test session)."""
     if not os.path.exists(B.HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path / "attn_fwd.s"
+    if "asm" in _ASM:
+        return _ASM["asm"]
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
-    r = subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), B.SRC],
-                       capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return out.read_text()
+    text = []
+    for src in B.SOURCES:
+        out = tmp_path / (os.path.basename(src) + ".s")
+        r = subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), src],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        text.append(out.read_text())
+    _ASM["asm"] = "\n".join(text)
+    return _ASM["asm"]
 
 
 def _instructions(asm):

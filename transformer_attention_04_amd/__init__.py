@@ -10,6 +10,7 @@ built, importing this package raises.
     attn_fwd_varlen(q, k, v, kv_lens, causal=False, ...)     -> o
     attn_fwd_splitkv(q, k, v, causal=False, n_split=0, ...)  -> o
     attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len)   -> kv_len + n
+    attn_qkv_proj(x, w, bias=None)                           -> (q, k, v)
     attn_strerror(status)                                    -> str
 
 q: [B, H, S_q, 64]; k, v: [B, H, S_kv, 64]; all contiguous, same dtype
@@ -32,7 +33,8 @@ STATUS = {
     9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH", 11: "ATTN_E_SPLIT", 12: "ATTN_E_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
-           "attn_splitkv_choose", "attn_kv_append", "attn_strerror", "attn_sched_grid", "attn_sched_tile")
+           "attn_splitkv_choose", "attn_kv_append", "attn_qkv_proj", "attn_strerror", "attn_sched_grid",
+           "attn_sched_tile")
 
 
 class AttnError(RuntimeError):
@@ -69,6 +71,8 @@ def _load(path: str = LIB_PATH):
     lib.attn_splitkv_workspace_bytes.restype = i
     lib.attn_splitkv_choose.argtypes = [i, i, i, i, i, ctypes.POINTER(i)]
     lib.attn_splitkv_choose.restype = i
+    lib.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.attn_qkv_proj.restype = i
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_kv_append.restype = i
     lib.attn_strerror.argtypes = [i]
@@ -242,6 +246,36 @@ def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, 
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o
+
+
+def attn_qkv_proj(x, w, bias=None, out=None, stream=None):
+    """Fused Q/K/V projection (see attn_qkv_proj in include/attn.h): x [B, S, d],
+    w [3d, d] (rows q, then k, then v; 64 rows per head), bias [3d] or None;
+    returns (q, k, v), each [B, H, S, 64] in x's dtype (bfloat16 or float16).
+    out: optional tuple of three such tensors to write."""
+    torch = _t()
+    for name, t in (("x", x), ("w", w)) + ((("bias", bias),) if bias is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.dtype != x.dtype or t.device != x.device:
+            raise ValueError(f"{name} must share x's dtype and device")
+    if x.dim() != 3 or x.shape[2] % 64:
+        raise ValueError(f"x must be [B, S, 64*H], got {tuple(x.shape)}")
+    B, S, d = x.shape
+    H = d // 64
+    if tuple(w.shape) != (3 * d, d) or (bias is not None and tuple(bias.shape) != (3 * d,)):
+        raise ValueError(f"w must be [{3 * d}, {d}] and bias [{3 * d}]")
+    outs = tuple(torch.empty((B, H, S, 64), dtype=x.dtype, device=x.device) for _ in range(3)) if out is None else out
+    for t in outs:
+        if tuple(t.shape) != (B, H, S, 64) or t.dtype != x.dtype or t.device != x.device or not t.is_contiguous():
+            raise ValueError("out tensors must be contiguous [B, H, S, 64] like x")
+    dev = x.device
+    st = _call(lib.attn_qkv_proj, dev, x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+               outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), B, S, H, 64, _dtype_code(x),
+               _stream_ptr(dev, stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return outs
 
 
 def attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len: int, stream=None) -> int:

@@ -10,6 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SOURCES = [SRC, os.path.join(PKG, "csrc", "qkv_proj.hip")]  # all linked into libattn.so
 OUT = os.path.join(PKG, "libattn.so")
 CLOCK_SRC = os.path.join(PKG, "csrc", "clock_probe.hip")
 CLOCK_OUT = os.path.join(PKG, "libattn_clock.so")
@@ -26,8 +27,9 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, out: str, extra: list[str] | None, verbose: bool) -> str:
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", out + ".tmp", src]
+def _compile(src, out: str, extra: list[str] | None, verbose: bool) -> str:
+    srcs = [src] if isinstance(src, str) else list(src)
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", out + ".tmp", *srcs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
     if r.returncode != 0:
@@ -64,7 +66,7 @@ def write_info() -> dict:
 def build(out: str = OUT, extra: list[str] | None = None, verbose: bool = False) -> str:
     """Build the attention library (and, for the default output path, the
     clock probe and the build record)."""
-    _compile(SRC, out, extra, verbose)
+    _compile(SOURCES, out, extra, verbose)
     if out == OUT:
         _compile(CLOCK_SRC, CLOCK_OUT, None, verbose)
         write_info()

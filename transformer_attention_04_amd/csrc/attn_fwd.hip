@@ -51,18 +51,10 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "gfx950.h"
+#include "host_common.h"
 
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int HEAD_DIM = 64;
 constexpr int BM = 128;        // query rows per workgroup
@@ -72,8 +64,6 @@ constexpr int SPLIT_MIN_KV_TILES = 16;   // the automatic split leaves shorter k
 constexpr int NTHREADS = 256;  // 4 wavefronts of 64
 constexpr float LAZY_TH = 8.0f;       // log2 headroom before the offset is raised
 constexpr float P_LIMIT = 32768.0f;  // largest per-lane block sum taken without a max
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // ---------------------------------------------------------------------------
 // Schedule: blockIdx.x -> (head, query rows [row0, row1)).
@@ -181,56 +171,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // extra vector instructions).
 __device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
-// from this lane's 64-bit address gsrc (a VGPR pair); lane l's bytes land at
-// LDS address m0 + 16*l, m0 wave-uniform.  Issued as inline assembly so the
-// compiler does not add its own conservative waits for it before unrelated
-// LDS reads; completion is tracked explicitly with wait_vmem (vmcnt counts
-// these copies, in issue order).  The compiler's hazard recognizer cannot see
-// inside the assembly, so the operands are chosen to need no help from it:
-// the address comes from VGPRs (a VMEM read of an SGPR written by a VALU
-// instruction would need wait states the compiler cannot insert here), and
-// the one wait state an SALU write of M0 needs before an LDS-DMA instruction
-// reads it is the s_nop inside the assembly.
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
-}
-
-// Two copies whose sources and destinations both lie 4096 bytes apart, from
-// one address and one M0 at their midpoint: the instruction offset (13-bit
-// signed) applies to the global and the LDS address alike, so the copies
-// take offsets -2048 and +2048.  Same operand rules as dma16.
-__device__ __forceinline__ void dma16_pair(const void* gmid, uint32_t m0mid) {
-  asm volatile(
-      "s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:-2048\n\tglobal_load_lds_dwordx4 %0, off offset:2048" ::"v"(gmid),
-      "{m0}"(m0mid)
-      : "memory");
-}
-
-// LDS byte address of a __shared__ location (what M0 takes).
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (the direct-to-LDS copies of later tiles may stay in flight).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));  // vmcnt=N, expcnt/lgkmcnt: no wait
-}
-
-// Workgroup barrier that does not drain in-flight direct-to-LDS copies (the
-// fence in __syncthreads would wait for all of them).  LDS reads of this wave
-// are complete before it arrives; the clobbers stop the compiler from moving
-// memory operations across it.
-__device__ __forceinline__ void barrier_keep_dma() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14) | (0x0 << 8));  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Online-softmax bookkeeping for one tile, shared by every element type.
 // s holds the raw scores of NB 32-key blocks (16 per lane per block, -inf where
 // masked).  Takes the row maximum (in-lane, then across the two half-waves),
@@ -277,47 +217,6 @@ __device__ __forceinline__ float online_offset(const f32x16 (&s)[NB], f32x16 (&a
 // ---------------------------------------------------------------------------
 // 16-bit element types
 // ---------------------------------------------------------------------------
-template <typename T>
-struct Half16;
-
-template <>
-struct Half16<__bf16> {
-  typedef bf16x8 vec8;
-  __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ unsigned pack2(float x, float y) {
-    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
-  }
-  // acc + w.x + w.y for a packed pair (v_dot2c_f32_bf16 against ones)
-  __device__ static __forceinline__ float add_pair(unsigned w, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-  }
-};
-
-template <>
-struct Half16<_Float16> {
-  typedef f16x8 vec8;
-  __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ unsigned pack2(float x, float y) {
-    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, f16x2));
-  }
-  // acc + w.x + w.y for a packed pair (v_dot2c_f32_f16 against ones)
-  __device__ static __forceinline__ float add_pair(unsigned w, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
-  }
-};
-
-// LDS tile of 64 rows x 128 bytes (64 16-bit values) = 8 KB.  16-byte chunks
-// are XOR-swizzled per row to keep the MFMA operand reads conflict-free.
-// K is read as one 16-byte chunk per lane, 16 consecutive rows per access.
-__device__ __forceinline__ int k16_off(int row, int c16) {
-  return row * 128 + ((c16 ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
-}
 // V is read with ds_read_b64_tr_b16: per 16-lane group, 4 consecutive rows x
 // 2 adjacent chunks; shifting the chunk pair by 2*(row & 3) spreads them over 8
 // distinct chunks.
@@ -1103,33 +1002,6 @@ __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const floa
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-// Per-device cache: 0 unknown, -1 not gfx950, else the compute-unit count.
-std::atomic<int> g_dev_cu[64];
-
-int check_device(int* n_cu) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_E_DEVICE;
-  if (dev < 64) {
-    const int s = g_dev_cu[dev].load(std::memory_order_relaxed);
-    if (s > 0) {
-      *n_cu = s;
-      return ATTN_OK;
-    }
-    if (s < 0) return ATTN_E_DEVICE;
-  }
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_E_DEVICE;
-  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.multiProcessorCount > 0;
-  if (dev < 64) g_dev_cu[dev].store(ok ? prop.multiProcessorCount : -1, std::memory_order_relaxed);
-  *n_cu = prop.multiProcessorCount;
-  return ok ? ATTN_OK : ATTN_E_DEVICE;
-}
-
-bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
-  const uint64_t pa = (uint64_t)(uintptr_t)a, pb = (uint64_t)(uintptr_t)b;
-  return pa < pb + nb && pb < pa + na;
-}
-
 int validate(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv,
              int D_h, int causal, float scale, int dtype, int chunk, int kv_len) {
   if (!q || !k || !v || !o) return ATTN_E_NULL;

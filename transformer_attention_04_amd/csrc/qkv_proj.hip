@@ -1,0 +1,253 @@
+// qkv_proj.hip -- fused Q/K/V projection for AMD Instinct MI355X (gfx950).
+//
+// The step upstream of attention: the layer input x [B, S, d] times the three
+// projection weights stacked as one linear-layer weight W [3d, d] (rows q,
+// then k, then v; 64 rows per head), plus an optional bias, as ONE matrix
+// product whose epilogue writes each 64-column head group straight into the
+// [B, H, S, 64] layout the attention kernels read (page "Roofline", sections
+// "What it does" and "How we built it": the Q/K/V projections fused into one
+// larger kernel).  No [B*S, 3d] intermediate exists.
+//
+// Work decomposition
+//   C = x W^T with M = B*S rows, N = 3d columns, K = d.  A workgroup of 8
+//   wavefronts owns a PM x PN = 256 x 256 tile of C and walks K in stages of
+//   PK = 64: per stage it copies the tile's 256 rows of x and 256 rows of W
+//   (128 bytes each) straight into LDS (global_load_lds_dwordx4, 16-byte
+//   chunks XOR-swizzled per row, the layout of the attention kernels' K
+//   tiles), two stages in flight-and-compute.  Both operands are contiguous
+//   in K, so the MFMA computes C^T = W x^T: lane l of a 32 x 32 block owns
+//   one row of C (row l % 32) and 16 of its columns, and the epilogue writes
+//   whole 8-byte pieces of output rows.  Wave (wm, wn) = (wave % 4, wave / 4)
+//   owns rows 64 wm .. +63 and columns 128 wn .. +127 of the tile: 2 x 4
+//   blocks of v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation (128
+//   accumulator registers of the 256 each of the two waves per SIMD has).
+//   Tiles are dealt so that the 12 (for d = 1024) column tiles of one row
+//   block run back to back on one XCD, which then reads that block of x from
+//   its own L2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "attn.h"
+#include "gfx950.h"
+#include "host_common.h"
+
+namespace {
+
+constexpr int PM = 256;                     // rows of x per workgroup
+constexpr int PN = 256;                     // rows of W (columns of C) per workgroup
+constexpr int PK = 64;                      // K per stage (one 128-byte row segment)
+constexpr int PTHREADS = 512;               // 8 wavefronts, two per SIMD
+constexpr int PROWB = PK * 2;               // bytes per staged row
+constexpr int PHALF = PM * PROWB;           // 32 KB: one stage of x (or of W)
+// LDS: x stage 0 | x stage 1 | W stage 0 | W stage 1.  Every operand read is
+// a per-lane base plus a constant below 64 KB (stage, block), which the
+// ds_read instruction takes as its immediate offset.
+constexpr int PLDS = 4 * PHALF;
+static_assert(PM == PN, "x and W stages share one size");
+
+template <typename T>
+struct ProjParams {
+  const T* x;     // [M, K]
+  const T* w;     // [N, K]
+  const T* bias;  // [N] or null
+  T* out[3];      // q, k, v: [B, H, S, 64]
+  int M, N, K;    // B*S, 3d, d
+  int S, H;
+  int tiles_n;    // column tiles
+  int tiles;      // total tiles
+};
+
+template <typename T>
+__global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) {
+  typedef Half16<T> H16;
+  typedef typename H16::vec8 vec8;
+  __shared__ __attribute__((aligned(16))) char lds[PLDS];
+
+  // Tile of this workgroup: with a multiple of 8 tiles, XCD x (blocks dealt
+  // round-robin) takes a contiguous run of tile indices, row block major.
+  int L = blockIdx.x;
+  if ((p.tiles & 7) == 0) L = (blockIdx.x & 7) * (p.tiles >> 3) + (blockIdx.x >> 3);
+  const int mt = L / p.tiles_n;
+  const int nt = L - mt * p.tiles_n;
+  const int m0 = mt * PM, n0 = nt * PN;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 31, hf = lane >> 5;
+  const int wm = wave & 3, wn = wave >> 2;
+
+  // Copies: wave w fills staged rows 32w .. +31 of x and of W, 8 rows per
+  // instruction; lane l lands in row r = 32w + 8i + l/8 at physical chunk
+  // l % 8 and fetches the logical chunk the row's swizzle maps there: with
+  // swizzle (r & 7) ^ ((r >> 3) & 1) = (l / 8) ^ (i & 1) that is chunk
+  // (l % 8) ^ (l / 8) ^ (i & 1).  Rows past the matrix end re-read its last
+  // row (finite data, never stored).  Source addresses are recomputed per
+  // copy rather than held in registers.
+  const int crow = 32 * wave + lane / 8;
+  const int cch = (lane % 8) ^ (lane / 8);
+  const char* const xb = reinterpret_cast<const char*>(p.x);
+  const char* const wb = reinterpret_cast<const char*>(p.w);
+  const int64_t rowb = (int64_t)p.K * 2;
+  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(32 * wave * PROWB));
+  auto issue = [&](int stage, int kt) {
+    const uint32_t mx = lds_addr(lds) + stage * PHALF + wdst, mw = mx + 2 * PHALF;
+    const int64_t off = (int64_t)kt * PROWB;
+    // An opaque copy of the row: otherwise the eight row addresses are hoisted
+    // out of the K loop and held (16 registers) for its whole length.
+    int row = crow;
+    asm volatile("" : "+v"(row));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row + 8 * i;
+      const int64_t col = off + 16 * (cch ^ (i & 1));
+      dma16(xb + min(m0 + r, p.M - 1) * rowb + col, mx + i * 8 * PROWB);
+      dma16(wb + min(n0 + r, p.N - 1) * rowb + col, mw + i * 8 * PROWB);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+
+  // Operand rows 64wm + 32mb + c (x) and 128wn + 32nb + c (W) all have the
+  // swizzle sw = (c & 7) ^ ((c >> 3) & 1), so k-step t (chunk 4hf + t, i.e.
+  // k = 32hf + 8t .. +7 in both operands) reads at a per-lane base plus
+  // stage * 32 KB + 4 KB per block.
+  // (32-bit LDS addresses: 8 registers for all eight bases.)
+  typedef __attribute__((address_space(3))) const char lchar;
+  typedef __attribute__((address_space(3))) const vec8 lvec8;
+  const int sw = (c & 7) ^ ((c >> 3) & 1);
+  lchar* const lbase = (lchar*)lds;
+  lchar* xa[4];
+  lchar* wa[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int ch = 16 * ((4 * hf + t) ^ sw);
+    xa[t] = lbase + (64 * wm + c) * PROWB + ch;
+    wa[t] = lbase + 2 * PHALF + (128 * wn + c) * PROWB + ch;
+  }
+  auto compute = [&](int stage) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      vec8 xo[2], wo[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) xo[mb] = *(lvec8*)(xa[t] + stage * PHALF + mb * 32 * PROWB);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) wo[nb] = *(lvec8*)(wa[t] + stage * PHALF + nb * 32 * PROWB);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = H16::mfma(wo[nb], xo[mb], acc[nb][mb]);
+    }
+  };
+
+  // Two stages: wait for stage kt (own copies), barrier (every wave's copies
+  // of kt have landed and every wave is done with kt - 1), start kt + 1 into
+  // kt - 1's buffer, compute kt.
+  const int n_k = p.K / PK;
+  issue(0, 0);
+  for (int kt = 0; kt < n_k; ++kt) {
+    wait_vmem<0>();
+    barrier_keep_dma();
+    if (kt + 1 < n_k) issue((kt + 1) & 1, kt + 1);
+    compute(kt & 1);
+  }
+
+  // Epilogue: block (nb, mb) register r holds C[m][n] with m = m0 + 64wm +
+  // 32mb + c and n = n0 + 128wn + 32nb + 8(r/4) + 4hf + r%4.  Blocks 2g and
+  // 2g+1 are the 64 columns n_g = n0 + 128wn + 64g .. +63: one head of one of
+  // q, k, v (d is a multiple of 64); registers 4gq .. 4gq+3 are 4 consecutive
+  // columns, stored as one 8-byte piece of the output row.
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int ng = n0 + 128 * wn + 64 * g;
+    if (ng >= p.N) continue;
+    const int which = ng / p.K;
+    const int h = (ng - which * p.K) >> 6;
+    T* const ob = p.out[which];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = m0 + 64 * wm + 32 * mb + c;
+      if (m >= p.M) continue;
+      const int bb = m / p.S, s = m - bb * p.S;
+      T* const orow = ob + (((int64_t)bb * p.H + h) * p.S + s) * 64;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f32x16& a = acc[2 * g + j][mb];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int e0 = 32 * j + 8 * gq + 4 * hf;
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (p.bias) {
+            const u32x2 braw = *reinterpret_cast<const u32x2*>(p.bias + ng + e0);
+            const T* bt = reinterpret_cast<const T*>(&braw);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = (float)bt[e];
+          }
+          const u32x2 wv = {H16::pack2(a[4 * gq] + bv[0], a[4 * gq + 1] + bv[1]),
+                            H16::pack2(a[4 * gq + 2] + bv[2], a[4 * gq + 3] + bv[3])};
+          *reinterpret_cast<u32x2*>(orow + e0) = wv;
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+int launch_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v, int B, int S, int H,
+                hipStream_t stream) {
+  ProjParams<T> p;
+  p.x = static_cast<const T*>(x);
+  p.w = static_cast<const T*>(w);
+  p.bias = static_cast<const T*>(bias);
+  p.out[0] = static_cast<T*>(q);
+  p.out[1] = static_cast<T*>(k);
+  p.out[2] = static_cast<T*>(v);
+  p.M = B * S;
+  p.K = 64 * H;
+  p.N = 3 * p.K;
+  p.S = S;
+  p.H = H;
+  p.tiles_n = (p.N + PN - 1) / PN;
+  p.tiles = ((p.M + PM - 1) / PM) * p.tiles_n;
+  hipLaunchKernelGGL((qkv_proj_kernel<T>), dim3(p.tiles), dim3(PTHREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v, int B,
+                             int S, int H, int D_h, int dtype, void* stream) {
+  if (!x || !w || !q || !k || !v) return ATTN_E_NULL;
+  if (B < 1 || S < 1 || H < 1 || D_h != 64) return ATTN_E_SHAPE;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  const int64_t M = (int64_t)B * S, d = 64 * (int64_t)H, N = 3 * d;
+  if (M > INT32_MAX || N > INT32_MAX) return ATTN_E_SHAPE;
+  if (M > INT64_MAX / (2 * d) || N > INT64_MAX / (2 * d)) return ATTN_E_SHAPE;
+  const int64_t tiles = ((M + PM - 1) / PM) * ((N + PN - 1) / PN);
+  if (tiles > INT32_MAX) return ATTN_E_SHAPE;
+  const uintptr_t mis = ((uintptr_t)x | (uintptr_t)w | (uintptr_t)bias | (uintptr_t)q | (uintptr_t)k |
+                         (uintptr_t)v) & 15u;
+  if (mis) return ATTN_E_ALIGN;
+  const uint64_t nx = (uint64_t)M * d * 2, nw = (uint64_t)N * d * 2, nb = bias ? (uint64_t)N * 2 : 0,
+                 no = (uint64_t)M * d * 2;  // each of q, k, v: B*H*S*64 elements
+  const void* outs[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    if (ranges_overlap(outs[i], no, x, nx) || ranges_overlap(outs[i], no, w, nw) ||
+        (bias && ranges_overlap(outs[i], no, bias, nb)))
+      return ATTN_E_OVERLAP;
+    for (int j = i + 1; j < 3; ++j)
+      if (ranges_overlap(outs[i], no, outs[j], no)) return ATTN_E_OVERLAP;
+  }
+  int n_cu = 0;
+  const int dv = check_device(&n_cu);
+  if (dv != ATTN_OK) return dv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_F16) return launch_proj<_Float16>(x, w, bias, q, k, v, B, S, H, s);
+  return launch_proj<__bf16>(x, w, bias, q, k, v, B, S, H, s);
+}
