@@ -59,6 +59,7 @@ CASES = [
     (2, 4, 1, 700, True, [700, 5]),             # one query row (decode)
     (6, 24, 520, 600, False, None),             # many query tiles: one wave group per tile
     (6, 24, 520, 600, True, None),
+    (70, 1, 130, 200, True, None),              # 70 sequences of one head each, lengths from 0 to 200
 ]
 
 
