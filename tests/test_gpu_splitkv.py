@@ -21,6 +21,7 @@ from parity import compare
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+DT_T = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def _lib():
@@ -122,3 +123,28 @@ def test_decode_step_of_the_long_cache():
     qs, ks, vs = (x[bs, hs].unsqueeze(0).cpu() for x in (q, k, v))   # [1, 16, S, 64]
     ref = oracle.attention(qs, ks, vs, causal=True)
     compare(o[bs, hs].unsqueeze(0).float().cpu().numpy(), ref, "bf16", "decode step")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_loop_append_then_split_attention(dtype):
+    """A decode loop on a growing cache: a 1000-row prefill, then 12 steps that
+    each append one K/V row (attn_kv_append) and attend that step's query
+    row to the grown cache with the automatic range count.  Every step is
+    checked against the oracle on the cache as it stands; rows past kv_len
+    hold NaN and must never be read."""
+    A = _lib()
+    B, H, cap, pre, steps = 2, 8, 1100, 1000, 12
+    q_all, k_all, v_all = _inputs(B, H, pre + steps, pre + steps, dtype, seed=41)
+    kc = torch.full((B, H, cap, 64), float("nan"), dtype=DT_T[dtype], device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    kv = A.attn_kv_append(kc, vc, k_all[:, :, :pre].contiguous().to(DEV), v_all[:, :, :pre].contiguous().to(DEV), 0)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for t in range(steps):
+        kv = A.attn_kv_append(kc, vc, k_all[:, :, kv:kv + 1].contiguous().to(DEV),
+                              v_all[:, :, kv:kv + 1].contiguous().to(DEV), kv)
+        q = q_all[:, :, kv - 1:kv].contiguous()
+        say(f"[decode loop] {dtype} step {t} kv_len={kv} n_split={A.splitkv_choose(B, H, 1, kv, n_cu)}")
+        o = A.attn_fwd_splitkv(q.to(DEV), kc, vc, causal=True, kv_len=kv)
+        torch.cuda.synchronize()
+        ref = oracle.attention(q, k_all[:, :, :kv], v_all[:, :, :kv], causal=True)
+        compare(o.float().cpu().numpy(), ref, dtype, f"decode step {t}")
