@@ -385,6 +385,12 @@ def main():
     torch.cuda.set_device(dev)
     footprint = w.bytes(dtype)
     n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
+    free_b, _ = torch.cuda.mem_get_info(dev)
+    if footprint > 0.9 * free_b:  # inputs and output of one set (plus the decode workspace, which is small)
+        print(f"bench.py: workload {w.name} needs {footprint / 2**30:.1f} GiB of device memory, "
+              f"{free_b / 2**30:.1f} GiB are free", file=sys.stderr)
+        sys.exit(3)
+    n_sets = max(1, min(n_sets, int(0.9 * free_b // footprint)))
     log(f"[bench] workload {w.name} dtype {dtype}: {footprint / 1e6:.1f} MB per set, {n_sets} sets")
     sets = []
     if w.S_q * w.S_kv * w.B * w.H > (1 << 32) or w.B * w.H * w.S_kv * w.D > (1 << 28):  # large: draw on the device
@@ -537,6 +543,9 @@ def main():
                    "aa_ratio": aa},
         "environment": environment(dev),
     }
+    alg_bytes = work[1] if work else w.bytes(dtype)
+    line["bandwidth"] = {"algorithmic_bytes": int(alg_bytes), "gbps": round(alg_bytes / sec / 1e9, 2),
+                         "note": "Q, K, V read once and O written once per call, over the measured time"}
     if args.varlen:
         line["config"]["kv_lens"] = lens_cpu.tolist()
     line["roofline"]["traffic"] = (None if (args.stream or args.varlen or args.decode)

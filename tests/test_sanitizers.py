@@ -1,0 +1,147 @@
+"""Address and undefined-behaviour sanitizer builds of the host code (CPU only).
+
+* The oracle (plain C) is linked with a small driver under
+  -fsanitize=address,undefined and run on regular, ragged, causal, partly
+  filled, row-subset and invalid calls.
+* The library's host code (argument validation, size and overflow checks,
+  schedule and workspace helpers, error strings) is compiled with the
+  sanitizers on the host side only; a driver calls every entry point with
+  invalid arguments (each returns its code before any HIP call) and the
+  host-only helpers over a range of sizes.  No GPU is used and no device
+  code is instrumented.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from transformer_attention_04_amd import build as B
+
+ORACLE_DRIVER = r"""
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+int oracle_attn_f64(const float *q, const float *k, const float *v, double *o,
+                    int64_t B, int64_t H, int64_t S_q, int64_t S_kv, int64_t D,
+                    int causal, double scale, int64_t kv_len,
+                    const int64_t *rows, int64_t n_rows, int n_threads);
+static float *rnd(int64_t n) {
+  float *p = (float *)malloc(sizeof(float) * (size_t)n);
+  for (int64_t i = 0; i < n; ++i) p[i] = (float)((i * 2654435761u) % 1000) / 500.0f - 1.0f;
+  return p;
+}
+int main(void) {
+  const int64_t shapes[][6] = {{1, 1, 1, 1, 1, 0}, {2, 3, 5, 9, 8, 1}, {1, 2, 17, 65, 64, 1}, {2, 1, 7, 7, 3, 0}};
+  int fails = 0;
+  for (int s = 0; s < 4; ++s) {
+    const int64_t B = shapes[s][0], H = shapes[s][1], Sq = shapes[s][2], Skv = shapes[s][3], D = shapes[s][4];
+    const int causal = (int)shapes[s][5];
+    float *q = rnd(B * H * Sq * D), *k = rnd(B * H * Skv * D), *v = rnd(B * H * Skv * D);
+    /* room for S_q rows, or for the two-row subset below, whichever is more */
+    double *o = (double *)malloc(sizeof(double) * (size_t)(B * H * (Sq > 2 ? Sq : 2) * D));
+    fails += oracle_attn_f64(q, k, v, o, B, H, Sq, Skv, D, causal, 0.3, Skv, NULL, Sq, 2) != 0;
+    const int64_t kvl = Skv > Sq ? Skv - 1 : Skv;
+    fails += oracle_attn_f64(q, k, v, o, B, H, Sq, Skv, D, causal, -0.7, kvl, NULL, Sq, 1) != 0;
+    int64_t rows[2] = {0, Sq - 1};
+    fails += oracle_attn_f64(q, k, v, o, B, H, Sq, Skv, D, causal, 1.0, Skv, rows, 2, 0) != 0;
+    /* invalid calls return an error and write nothing */
+    fails += oracle_attn_f64(q, k, v, o, B, H, Sq, Skv, D, causal, 1.0, Skv + 1, NULL, Sq, 1) == 0;
+    int64_t bad[1] = {Sq};
+    fails += oracle_attn_f64(q, k, v, o, B, H, Sq, Skv, D, causal, 1.0, Skv, bad, 1, 1) == 0;
+    free(q); free(k); free(v); free(o);
+  }
+  printf("oracle driver failures: %d\n", fails);
+  return fails != 0;
+}
+"""
+
+ABI_DRIVER = r"""
+#include <stdint.h>
+#include <stdio.h>
+#include "attn.h"
+int main(void) {
+  int fails = 0;
+  void *Q = (void *)0x100000, *K = (void *)0x200000, *V = (void *)0x300000, *O = (void *)0x400000;
+  /* invalid arguments: each returns its code before any HIP call */
+  fails += attn_fwd(0, K, V, O, 2, 3, 100, 120, 64, 1, 0.125f, 2, 0) != ATTN_E_NULL;
+  fails += attn_fwd(Q, K, V, O, 2, 3, 100, 120, 32, 1, 0.125f, 2, 0) != ATTN_E_SHAPE;
+  fails += attn_fwd(Q, K, V, O, 1 << 20, 1 << 12, 100, 120, 64, 1, 0.125f, 2, 0) != ATTN_E_SHAPE;
+  fails += attn_fwd(Q, K, V, O, 1 << 14, 1 << 14, 1 << 20, 1 << 20, 64, 1, 0.125f, 2, 0) != ATTN_E_SHAPE;
+  fails += attn_fwd_chunked(Q, K, V, O, 2, 3, 100, 120, 64, 1, 0.125f, 2, 0, 0, 120) != ATTN_E_CHUNK;
+  fails += attn_fwd_chunked(Q, K, V, O, 2, 3, 121, 120, 64, 1, 0.125f, 2, 0, 64, 120) != ATTN_E_CAUSAL;
+  fails += attn_fwd_varlen(Q, K, V, O, 2, 3, 100, 120, 64, 1, 0.125f, 2, 0, 0) != ATTN_E_NULL;
+  fails += attn_fwd_splitkv(Q, K, V, O, 2, 3, 100, 120, 64, 1, 0.125f, 2, 0, 120, 0, 0, 0) != ATTN_E_SPLIT;
+  fails += attn_fwd_splitkv(Q, K, V, O, 2, 3, 100, 120, 64, 1, 0.125f, 2, 0, 120, 4, 0, 0) != ATTN_E_WORKSPACE;
+  fails += attn_kv_append(K, V, Q, O, 2, 3, 100, 90, 20, 64, 2, 0) != ATTN_E_SHAPE;
+  fails += attn_qkv_proj(Q, K, 0, V, O, (void *)0x500000, 2, 100, 4, 64, 0, 0) != ATTN_E_DTYPE;
+  fails += attn_qkv_proj(Q, K, 0, Q, O, (void *)0x500000, 2, 100, 4, 64, 2, 0) != ATTN_E_OVERLAP;
+  /* host-only helpers over a range of sizes */
+  for (int B = 1; B <= 64; B *= 4)
+    for (int S = 1; S <= 100000; S *= 7) {
+      size_t bytes = 0;
+      int n = 0, grid = 0, head = 0, r0 = 0, r1 = 0;
+      fails += attn_splitkv_choose(B, 16, S < 512 ? S : 1, S, 256, &n) != ATTN_OK;
+      fails += attn_splitkv_workspace_bytes(B, 16, S < 512 ? S : 1, n, &bytes) != ATTN_OK;
+      fails += attn_sched_grid(B, 16, S, 4096, S, 1, &grid) != ATTN_OK;
+      fails += attn_sched_tile(B, 16, S, 4096, S, 1, grid - 1, &head, &r0, &r1) != ATTN_OK;
+      fails += !(r0 < r1 && r1 <= S);
+    }
+  for (int c = -1; c < 14; ++c) fails += attn_strerror(c) == 0;
+  printf("abi driver failures: %d\n", fails);
+  return fails != 0;
+}
+"""
+
+
+def _run(cmd, **kw):
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, **kw)
+    return r
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    drv = tmp_path / "drv.c"
+    drv.write_text(ORACLE_DRIVER)
+    exe = tmp_path / "oracle_san"
+    src = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+    r = _run(["gcc", "-O1", "-g", "-fopenmp", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-o", str(exe), str(drv), src, "-lm"])
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1")
+    r = _run([str(exe)], env=env)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "failures: 0" in r.stdout
+
+
+def test_library_host_code_under_sanitizers(tmp_path):
+    if not os.path.exists(B.HIPCC):
+        pytest.skip("hipcc not available")
+    clang = os.path.join(os.path.dirname(os.path.realpath(B.HIPCC)), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC", "-O3")]
+    objs = []
+    for src in B.SOURCES:  # sanitizers on the host side of each HIP source only
+        obj = tmp_path / (os.path.basename(src) + ".o")
+        r = _run([B.HIPCC, *flags, "-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                  "-fsanitize=undefined", "-c", src, "-o", str(obj)])
+        assert r.returncode == 0, r.stderr[-3000:]
+        objs.append(str(obj))
+    drv = tmp_path / "drv.c"
+    drv.write_text(ABI_DRIVER)
+    dobj = tmp_path / "drv.o"
+    r = _run([clang, "-O1", "-g", "-I", os.path.join(B.ROOT, "include"), "-fsanitize=address,undefined", "-c",
+              str(drv), "-o", str(dobj)])
+    assert r.returncode == 0, r.stderr[-3000:]
+    exe = tmp_path / "abi_san"
+    r = _run([B.HIPCC, "--offload-arch=gfx950", "-fno-gpu-sanitize", "-fsanitize=address,undefined",
+              "-o", str(exe), *objs, str(dobj)])
+    assert r.returncode == 0, r.stderr[-3000:]
+    # leaks inside the HIP runtime's own start-up are not this library's
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = _run([str(exe)], env=env)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "failures: 0" in r.stdout
