@@ -33,9 +33,10 @@
  * Arithmetic: Q K^T and P V run on MFMA (bf16/fp16 operands with fp32
  * accumulation for ATTN_BF16/ATTN_F16; true fp32 MFMA for ATTN_F32).  The
  * probabilities P are computed in fp32; on the 16-bit paths they are rounded
- * once to the input type, and both the P V product and the row sum l use those
- * rounded values (l is accumulated in fp32), so the normalised weights sum to
- * one up to fp32 rounding.  No [S_q, S_kv] buffer is written anywhere.
+ * once to the input type, only as the operand of the P V product, and the row
+ * sum l adds the fp32 values before that rounding (so the normalised weights
+ * sum to one within the rounding of P: a relative 2^-9 for bf16, 2^-12 for
+ * fp16).  No [S_q, S_kv] buffer is written anywhere.
  *
  * Ownership and concurrency: the caller allocates and frees every buffer.  The
  * library allocates no device or host memory, keeps no pointer after it

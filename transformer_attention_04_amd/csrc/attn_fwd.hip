@@ -37,11 +37,10 @@
 // (then acc and l are rescaled by exp2(m_old - m_new)).  Steady-state blocks
 // therefore need neither the row maximum nor a rescale, and every probability
 // fed to the P V product is <= 2^15, inside the fp16 range.  Probabilities are
-// rounded to bf16/fp16 as the MFMA operand of the P V product and l sums the
-// same rounded values (so O is an exact weighted mean of the V rows with those
-// weights).  fp32 inputs keep fp32 probabilities and take the maximum on every
-// block (their fp32 MFMAs dominate; the lazy 2^8 rule still skips most
-// rescales).
+// rounded to bf16/fp16 only as the MFMA operand of the P V product; l sums
+// them in fp32 before that rounding.  fp32 inputs keep fp32 probabilities and
+// take the maximum on every block (their fp32 MFMAs dominate; the lazy 2^8
+// rule still skips most rescales).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -227,12 +226,16 @@ __device__ __forceinline__ int v16_off(int row, int c16) {
 // Probabilities of one tile for the 16-bit path: P = exp2(s*c - moff) in fp32,
 // RNE-packed to 16 bits in the B-operand layout of the P V product (pw[kb][u]
 // word q holds keys 8u + 2q, 8u + 2q + 1 of block kb, k-slots 8hf + 2q, +1).
-// Returns this lane's sum of the packed (rounded) values.
+// Returns this lane's sum of the fp32 values, taken with plain fp32 adds: the
+// packed-pair dot instructions would halve the count, but on gfx950 they wait
+// for the matrix pipe, so while the other wave of the SIMD streams MFMAs they
+// stall this wave's whole in-order instruction stream (fma, exp, cvt and add
+// all run beside the MFMAs).
 template <typename T, int NB>
 __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, const float moff,
                                          u32x4 (&pw)[NB][2]) {
   typedef Half16<T> H;
-  float ls[2] = {0.f, 0.f};  // independent partial sums
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -242,11 +245,11 @@ __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, 
         const int r = 8 * u + 2 * q;
         const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
         const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
-        const unsigned w = H::pack2(e0, e1);
-        pw[kb][u][q] = w;
-        ls[q & 1] = H::add_pair(w, ls[q & 1]);
+        pw[kb][u][q] = H::pack2(e0, e1);
+        ls[2 * (q & 1)] += e0;
+        ls[2 * (q & 1) + 1] += e1;
       }
-  return ls[0] + ls[1];
+  return (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
 // One wave's work on one 64-key tile: S^T = K Q^T on MFMA, online-softmax
@@ -295,30 +298,6 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
   f32x16 s[NB];
   scores(s, kv0);
 
-  // V^T operands, read transposed from the [key][d] tile before the softmax
-  // so their latency overlaps it.  Operand (kb, u, dt), k-slot 8hf + e, holds
-  // V[32kb + 16u + 8(e/4) + 4hf + e%4][32dt + c]: source lane s of each
-  // 16-lane group reads row kbase + s/4, columns d0 + 4(s%4) .. +3.
-  vec8 va[NB][2][2];
-  {
-    const int g = lane >> 4, sl = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
-          const int c16 = d0 >> 3, half = (d0 >> 2) & 1;
-          const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row + 8, c16) + 8 * half));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          va[kb][u][dt] = __builtin_bit_cast(vec8, aw);
-        }
-  }
-
   // Take the probabilities at the current offset.  If some lane's offset is
   // not set yet (m = -inf: its row has seen no key) or its block sum is out
   // of range, redo the tile through the maximum: re-read K (s is consumed by
@@ -346,6 +325,32 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
     ts = probs16<T, NB>(s, cc, moff, pw);
   }
   l += ts;
+
+  // V^T operands, read transposed from the [key][d] tile after the softmax:
+  // not live during it, the 16-bit kernel fits three workgroups per CU (168
+  // VGPRs), whose third wave per SIMD hides the reads' latency.  Operand
+  // (kb, u, dt), k-slot 8hf + e, holds
+  // V[32kb + 16u + 8(e/4) + 4hf + e%4][32dt + c]: source lane s of each
+  // 16-lane group reads row kbase + s/4, columns d0 + 4(s%4) .. +3.
+  vec8 va[NB][2][2];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+          const int c16 = d0 >> 3, half = (d0 >> 2) & 1;
+          const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row + 8, c16) + 8 * half));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          va[kb][u][dt] = __builtin_bit_cast(vec8, aw);
+        }
+  }
 
   // O^T += V^T P^T: step (kb, u) contracts keys 32kb + 16u .. +15.
 #pragma unroll
@@ -477,8 +482,10 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 // SPLIT: the workgroup covers one key range of its query rows (the cache is
 // viewed from the range's first row on, with the causal shift of the whole
 // cache) and writes the partial (m, l, acc) instead of O.
+// Occupancy: three four-wave 16-bit workgroups per CU (48 KB of LDS and at
+// most 168 VGPRs each), else one or two.
 template <typename T, bool CAUSAL, int KS, bool VARLEN, bool SPLIT>
-__global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 2 : 1)
+__global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3 : 1)
     attn_fwd_kernel(Params<T> p) {
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ROWB = F32 ? 256 : 128;  // bytes per K/V row (64 elements)
@@ -1095,8 +1102,9 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   p.base_grid = grid;
   if (n_split > 1) {
     // Split the keys into n_split ranges of whole 64-key tiles; the four-wave
-    // workgroup runs every range (two per CU keep more tile copies in flight
-    // than one eight-wave workgroup).  Ranges past the last tile are empty.
+    // workgroup runs every range (several per CU keep more tile copies in
+    // flight than one eight-wave workgroup).  Ranges past the last tile are
+    // empty.
     const int kv_tiles = (kv_len + BN - 1) / BN;
     const int per = (kv_tiles + n_split - 1) / n_split;
     p.split_span = per * BN;

@@ -83,11 +83,6 @@ struct Half16<__bf16> {
   __device__ static __forceinline__ unsigned pack2(float x, float y) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
   }
-  // acc + w.x + w.y for a packed pair (v_dot2c_f32_bf16 against ones)
-  __device__ static __forceinline__ float add_pair(unsigned w, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-  }
 };
 
 template <>
@@ -98,11 +93,6 @@ struct Half16<_Float16> {
   }
   __device__ static __forceinline__ unsigned pack2(float x, float y) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, f16x2));
-  }
-  // acc + w.x + w.y for a packed pair (v_dot2c_f32_f16 against ones)
-  __device__ static __forceinline__ float add_pair(unsigned w, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
   }
 };
 
