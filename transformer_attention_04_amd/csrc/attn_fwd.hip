@@ -909,23 +909,27 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
     return;
   }
   const float inv = (lt > 0.f) ? 1.0f / lt : 0.f;
-  // An opaque lane index: the store rows below equal the Q copy rows of the
-  // prologue, which the compiler would otherwise keep live across the loop.
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
+  // Lane, column, half-wave and wave indices recomputed from an opaque copy
+  // of the thread index: the staging offsets and store rows below equal
+  // values the prologue computed, which the compiler would otherwise keep
+  // live across the key loop (or spill, at three workgroups per CU).
+  int tx = threadIdx.x;
+  asm volatile("" : "+v"(tx));
+  const int ln = tx & 63;
+  const int ec = ln & 31, ehf = ln >> 5;
   char* ot;
   if constexpr (KS == 1) {
     const int os = (n_super + 1) % 3;
-    ot = (os == 0 ? st0 : os == 1 ? st1 : st2) + wave * (32 * ROWB);
+    ot = (os == 0 ? st0 : os == 1 ? st1 : st2) + (tx >> 6) * (32 * ROWB);
   } else {
-    ot = st0 + qg * (8 * 64 * 16);
+    ot = st0 + ((tx >> 6) & 3) * (8 * 64 * 16);
   }
   if constexpr (F32) {
     // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
     // 4g .. 4g+3 of both accumulators cover columns 16g + 8hf .. +7.
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int ch = 4 * gq + 2 * hf;  // 16-byte chunk of columns 16g + 8hf .. +3
+      const int ch = 4 * gq + 2 * ehf;  // 16-byte chunk of columns 16g + 8hf .. +3
       u32x4 w0, w1;
       w0[0] = __float_as_uint(acc[0][4 * gq] * inv);
       w0[1] = __float_as_uint(acc[1][4 * gq] * inv);
@@ -935,8 +939,8 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
       w1[1] = __float_as_uint(acc[1][4 * gq + 2] * inv);
       w1[2] = __float_as_uint(acc[0][4 * gq + 3] * inv);
       w1[3] = __float_as_uint(acc[1][4 * gq + 3] * inv);
-      *reinterpret_cast<u32x4*>(ot + c * 256 + 16 * (ch ^ (c & 15))) = w0;
-      *reinterpret_cast<u32x4*>(ot + c * 256 + 16 * ((ch + 1) ^ (c & 15))) = w1;
+      *reinterpret_cast<u32x4*>(ot + ec * 256 + 16 * (ch ^ (ec & 15))) = w0;
+      *reinterpret_cast<u32x4*>(ot + ec * 256 + 16 * ((ch + 1) ^ (ec & 15))) = w1;
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {  // rows 4k .. 4k+3
@@ -955,7 +959,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
         u32x2 w;
         w[0] = H::pack2(acc[dt][4 * gq] * inv, acc[dt][4 * gq + 1] * inv);
         w[1] = H::pack2(acc[dt][4 * gq + 2] * inv, acc[dt][4 * gq + 3] * inv);
-        *reinterpret_cast<u32x2*>(ot + c * 128 + 16 * ((4 * dt + gq) ^ (c & 7)) + 8 * hf) = w;
+        *reinterpret_cast<u32x2*>(ot + ec * 128 + 16 * ((4 * dt + gq) ^ (ec & 7)) + 8 * ehf) = w;
       }
     }
 #pragma unroll
