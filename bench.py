@@ -17,6 +17,7 @@ Default workload: multi-head non-causal S=512 (B=8, H=8, D=64) in fp32.
 from __future__ import annotations
 
 import argparse
+import statistics
 import json
 import math
 import os
@@ -230,6 +231,63 @@ def gpu_clock_mhz(dev, n_wg=256, iters=4096):
     c = out.view(n_wg, 2).cpu().double()
     mhz = 100.0 * c[:, 0] / c[:, 1].clamp(min=1)
     return round(float(mhz.median()), 1)
+
+
+def measured_peak(dev, bound, dtype):
+    """The ceiling this box sustains for the roof that binds: a pure MFMA loop
+    (attn_mfma_probe, two waves per SIMD, 16 MFMAs per iteration in four
+    chains) in TFLOP/s, or a 1 GiB streaming copy (attn_copy_probe, read +
+    write) in GB/s.  Median of 5 timed launches after one warmup.  None if the
+    probe library is missing."""
+    import ctypes
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    if bound == "mfma":
+        path = os.path.join(ROOT, "transformer_attention_04_amd", "libattn_clock.so")
+        if not os.path.exists(path):
+            return None
+        lib = ctypes.CDLL(path)
+        lib.attn_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+        n_wg = 2 * torch.cuda.get_device_properties(dev).multi_processor_count  # 8 waves per CU
+        iters = 32768 if code else 8192  # ~15-20 ms per launch: long enough for the clock to settle
+        out = torch.empty(4 * n_wg, dtype=torch.float32, device=dev)
+        flops = n_wg * 4 * iters * 16 * (4096 if code == 0 else 32768)
+        for r in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.attn_mfma_probe(out.data_ptr(), n_wg, iters, code, ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            if st != 0:
+                return None
+            torch.cuda.synchronize(dev)
+            if r:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        return {"peak": round(flops / statistics.median(times) / 1e12, 1), "unit": "TFLOP/s",
+                "how": f"{dtype} 32x32 MFMA loop, 4 chains, 2 waves per SIMD (attn_mfma_probe)"}
+    path = os.path.join(ROOT, "transformer_attention_04_amd", "libattn_clock.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.attn_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    n_wg = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    for r in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.attn_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, n_wg, ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if st != 0:
+            return None
+        torch.cuda.synchronize(dev)
+        if r:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return {"peak": round(2 * nbytes / statistics.median(times) / 1e9, 1), "unit": "GB/s",
+            "how": "streaming copy of 1 GiB, 16 B per lane, bytes read + written (attn_copy_probe)"}
 
 
 def environment(dev):
@@ -550,6 +608,13 @@ def main():
         line["config"]["kv_lens"] = lens_cpu.tolist()
     line["roofline"]["traffic"] = (None if (args.stream or args.varlen or args.decode)
                                    else measured_traffic(w.name, dtype))
+    # The datasheet peak is the headline; the ceiling measured on this machine is
+    # reported beside it, labelled.
+    mp = measured_peak(dev, line["roofline"]["bound"], dtype)
+    if mp is not None:
+        mp["frac"] = round(line["roofline"]["achieved"] / mp["peak"], 4)
+    line["roofline"]["peak_source"] = "datasheet"
+    line["roofline"]["measured"] = mp
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)

@@ -50,6 +50,34 @@ def test_clock_probe_library_exports_and_checks_arguments():
     assert f(0x1000, 1, (1 << 24) + 1, None) == 2
 
 
+def test_mfma_probe_checks_arguments_before_any_launch():
+    lib = ctypes.CDLL(CLOCK_LIB)
+    f = lib.attn_mfma_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 1, 1, 2, None) == 1
+    assert f(0x1002, 1, 1, 2, None) == 1     # not 4-byte aligned
+    assert f(0x1000, 0, 1, 2, None) == 2
+    assert f(0x1000, 65537, 1, 2, None) == 2
+    assert f(0x1000, 1, 0, 2, None) == 2
+    assert f(0x1000, 1, (1 << 24) + 1, 2, None) == 2
+    assert f(0x1000, 1, 1, 3, None) == 2     # unknown dtype code
+    assert f(0x1000, 1, 1, -1, None) == 2
+
+
+def test_copy_probe_checks_arguments_before_any_launch():
+    lib = ctypes.CDLL(CLOCK_LIB)
+    f = lib.attn_copy_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 0x2000, 16, 1, None) == 1
+    assert f(0x1000, None, 16, 1, None) == 1
+    assert f(0x1008, 0x9000, 16, 1, None) == 1     # not 16-byte aligned
+    assert f(0x1000, 0x9000, 0, 1, None) == 2
+    assert f(0x1000, 0x9000, 24, 1, None) == 2     # not a multiple of 16
+    assert f(0x1000, 0x9000, 16, 0, None) == 2
+    assert f(0x1000, 0x9000, 16, 65537, None) == 2
+    assert f(0x1000, 0x1010, 64, 1, None) == 2     # overlapping ranges
+
+
 def test_multi_gpu_request_exits_with_a_message():
     import subprocess
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
