@@ -272,8 +272,11 @@ def measured_peak(dev, bound, dtype):
     lib = ctypes.CDLL(path)
     lib.attn_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     nbytes = 1 << 30
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
+    try:
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+    except torch.cuda.OutOfMemoryError:
+        return None
     n_wg = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
     for r in range(6):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -397,7 +400,7 @@ def bench_qkv(args, w, dtype):
                    "launch": "hip_graph_replay" if graphs else "eager"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": pk, "unit": "TFLOP/s",
                      "frac": round(tflops / pk, 4), "traffic": None,
-                     "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes, "peak_source": "datasheet"},
         "timing": {"repeats": len(rep_ms), "steps_per_repeat": sizes,
                    "ms_per_step_each_repeat": [round(x, 6) for x in rep_ms],
                    "median_ms_per_step": round(sorted(rep_ms)[len(rep_ms) // 2], 6),
@@ -405,6 +408,10 @@ def bench_qkv(args, w, dtype):
         "environment": environment(dev),
         "cpu_baseline": None,
     }
+    mp = measured_peak(dev, "mfma", dtype)
+    if mp is not None:
+        mp["frac"] = round(tflops / mp["peak"], 4)
+    line["roofline"]["measured"] = mp
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
