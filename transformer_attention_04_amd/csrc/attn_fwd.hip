@@ -14,7 +14,9 @@
 // Work decomposition (both element types)
 //   workgroup = 4 wavefronts x 32 query rows = BM = 128 rows of one (b, h);
 //   per iteration the workgroup stages BN = 64 keys of K and V in LDS
-//   (double-buffered, 128-bit coalesced global loads issued one tile ahead);
+//   (direct global-to-LDS copies, 16 bytes per lane, into three stages issued
+//   two tiles ahead -- two stages, one ahead, when two wave groups split the
+//   keys);
 //   each wave computes S^T = K Q^T on MFMA so that a lane owns ONE query row
 //   (lane % 32) and 16 keys per 32-key block: the row max and row sum are
 //   in-lane plus one exchange between the two half-waves (v_permlane32_swap);
