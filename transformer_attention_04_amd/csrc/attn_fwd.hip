@@ -563,22 +563,30 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // super-tile's (scalar) offset; only a super-tile that crosses the cache
   // end computes clamped rows (rows past kv_len - 1 re-read row kv_len - 1:
   // finite data, and those keys are masked).
-  int crow[NCP];
-  uint32_t kcb[NCP], vcb[NCP], kof[NCP], vof[NCP];
+  // Stage row of copy i of the wave of thread t, and the byte offsets of the
+  // lane's 16-byte chunk in a K row and a V row (swizzled).  The clamped
+  // copies recompute these from an opaque copy of the thread index, so none
+  // of them stays live across the key loop.
+  auto copy_geom = [&](const int i, const int t, int& row, uint32_t& kc, uint32_t& vc) {
+    const int ln = t & 63, wv = t >> 6;
+    row = 64 * (wv >> 2) + RPC * (4 * i + (wv & 3)) + ln / LPR;
+    const int ph = ln % LPR;
+    if constexpr (F32) {
+      kc = 16 * (ph ^ (row & 15));
+      vc = 16 * ph;
+    } else {
+      kc = 16 * (ph ^ ((row & 7) ^ ((row >> 3) & 1)));
+      vc = 16 * (ph ^ ((row & 3) << 1));
+    }
+  };
+  uint32_t kof[NCP], vof[NCP];
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
-    const int row = 64 * kh + RPC * (4 * i + qg) + lane / LPR;
-    const int ph = lane % LPR;
-    crow[i] = row;
-    if constexpr (F32) {
-      kcb[i] = 16 * (ph ^ (row & 15));
-      vcb[i] = 16 * ph;
-    } else {
-      kcb[i] = 16 * (ph ^ ((row & 7) ^ ((row >> 3) & 1)));
-      vcb[i] = 16 * (ph ^ ((row & 3) << 1));
-    }
-    kof[i] = (uint32_t)row * ROWB + kcb[i];
-    vof[i] = (uint32_t)row * ROWB + vcb[i];
+    int row;
+    uint32_t kc, vc;
+    copy_geom(i, tid, row, kc, vc);
+    kof[i] = (uint32_t)row * ROWB + kc;
+    vof[i] = (uint32_t)row * ROWB + vc;
   }
   const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)((64 * kh + RPC * qg) * ROWB));
   const char* kbase = reinterpret_cast<const char*>(kh_ptr);
@@ -610,11 +618,16 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
       issue_full(st, super);
     } else {
       const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
+      int tx = threadIdx.x;
+      asm volatile("" : "+v"(tx));
 #pragma unroll
       for (int i = 0; i < NCP; ++i) {
-        const uint32_t rb = (uint32_t)min(kv0 + crow[i], kv_len - 1) * ROWB;
-        dma16(kbase + (rb + kcb[i]), mk + i * CSTEP);
-        dma16(vbase + (rb + vcb[i]), mv + i * CSTEP);
+        int row;
+        uint32_t kc, vc;
+        copy_geom(i, tx, row, kc, vc);
+        const uint32_t rb = (uint32_t)min(kv0 + row, kv_len - 1) * ROWB;
+        dma16(kbase + (rb + kc), mk + i * CSTEP);
+        dma16(vbase + (rb + vc), mv + i * CSTEP);
       }
     }
   };
