@@ -85,7 +85,10 @@ def test_varlen_matches_oracle(dtype):
 @pytest.mark.parametrize("causal", [False, True])
 def test_equal_lengths_equal_chunked_bitwise(dtype, causal):
     A = _lib()
-    for B, H, S_q, S_kv, L in ((2, 3, 257, 400, 333), (8, 16, 512, 600, 530)):  # L >= S_q: chunked needs it when causal
+    # L >= S_q: chunked needs it when causal.  The third shape has more than
+    # two 128-row query tiles per CU (the one-group kernel at three workgroups
+    # per CU), a partial last query tile and a partial cache-end tile.
+    for B, H, S_q, S_kv, L in ((2, 3, 257, 400, 333), (8, 16, 512, 600, 530), (4, 16, 1100, 1300, 1250)):
         say(f"[varlen=chunked] {dtype} causal={causal} B={B} H={H} S_q={S_q} S_kv={S_kv} L={L}")
         q, k, v = (x.to(DEV) for x in _inputs(B, H, S_q, S_kv, dtype, seed=31))
         lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
