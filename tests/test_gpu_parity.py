@@ -184,6 +184,21 @@ def test_chunked_equals_unchunked_bitwise(dtype):
             assert torch.equal(o, ref), f"chunk {chunk} causal {causal} differs"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_chunked_equals_unchunked_bitwise_many_tiles(dtype):
+    # More than two 128-row query tiles per CU: the one-group kernel at three
+    # workgroups per CU; windows that do and do not align with query tiles.
+    w = W.Workload("chunk_many", 8, 16, 700, 700, 64, True, (dtype,), seed=13)
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, dtype))
+    A = _lib()
+    for causal in (True, False):
+        ref = A.attn_fwd(q, k, v, causal=causal)
+        for chunk in (64, 128, 300, 699, 4096):
+            say(f"[chunk many] {dtype} causal={causal} chunk={chunk}")
+            o = A.attn_fwd_chunked(q, k, v, chunk=chunk, causal=causal)
+            assert torch.equal(o, ref), f"chunk {chunk} causal {causal} differs"
+
+
 def test_streaming_windows_equal_single_call():
     """Window-by-window calls with a growing kv_len give the single call's rows."""
     A = _lib()
