@@ -74,9 +74,9 @@ enum attn_status {
     ATTN_E_CAUSAL = 5,   /* causal with S_q > kv_len (a row would see no key) */
     ATTN_E_CHUNK = 6,    /* chunk < 1, or kv_len outside [1, S_kv] */
     ATTN_E_ALIGN = 7,    /* a base pointer is not 16-byte aligned */
-    ATTN_E_OVERLAP = 8,  /* o overlaps q, k or v */
-    ATTN_E_DEVICE = 9,   /* no current HIP device, or it is not gfx950 */
-    ATTN_E_LAUNCH = 10,  /* the kernel launch reported an error */
+    ATTN_E_DEVICE = 8,   /* no current HIP device, or it is not gfx950 */
+    ATTN_E_HIP = 9,      /* the HIP runtime reported an error for the launch */
+    ATTN_E_OVERLAP = 10, /* o overlaps q, k or v */
     ATTN_E_SPLIT = 11,   /* n_split outside [1, 1024], or the split grid exceeds 2^31 - 1 workgroups */
     ATTN_E_WORKSPACE = 12 /* workspace NULL, not 16-byte aligned, smaller than required, or overlapping q/k/v/o */
 };
@@ -213,7 +213,7 @@ int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, int *n_spli
  * `stream`, nothing allocated).  Errors: ATTN_E_NULL (x, w, q, k or v NULL);
  * ATTN_E_SHAPE (B, S or H < 1, D_h != 64, sizes overflow); ATTN_E_DTYPE
  * (ATTN_F32 or unknown); ATTN_E_ALIGN; ATTN_E_OVERLAP (an output overlaps an
- * input or another output); ATTN_E_DEVICE; ATTN_E_LAUNCH.
+ * input or another output); ATTN_E_DEVICE; ATTN_E_HIP.
  */
 int attn_qkv_proj(const void *x, const void *w, const void *bias,
                   void *q, void *k, void *v,
@@ -237,7 +237,7 @@ int attn_qkv_proj(const void *x, const void *w, const void *bias,
  * S_cap or n_new < 1, kv_len < 0, kv_len + n_new > S_cap, D_h != 64, sizes
  * overflow); ATTN_E_DTYPE; ATTN_E_ALIGN; ATTN_E_OVERLAP (the two caches
  * overlap, or a new-rows buffer overlaps a cache); ATTN_E_DEVICE;
- * ATTN_E_LAUNCH.
+ * ATTN_E_HIP.
  */
 int attn_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                    int B, int H, int S_cap, int kv_len, int n_new, int D_h,

@@ -38,6 +38,21 @@ def test_status_codes_match_header():
         assert m and int(m.group(1)) == code, name
 
 
+def test_status_numbering_follows_the_boundary_contract():
+    """The numbering of the documented boundary: the first ten codes, in
+    order, with the device check at 8 and a HIP runtime error at 9; the
+    codes of the extra entry points come after them."""
+    want = ["ATTN_OK", "ATTN_E_NULL", "ATTN_E_SHAPE", "ATTN_E_DTYPE", "ATTN_E_SCALE", "ATTN_E_CAUSAL",
+            "ATTN_E_CHUNK", "ATTN_E_ALIGN", "ATTN_E_DEVICE", "ATTN_E_HIP"]
+    for code, name in enumerate(want):
+        assert A.STATUS[code] == name and getattr(A, name) == code
+    assert min(A.ATTN_E_OVERLAP, A.ATTN_E_SPLIT, A.ATTN_E_WORKSPACE) >= 10
+
+
+def test_short_binding_names_are_the_entry_points():
+    assert A.fwd is A.attn_fwd and A.fwd_chunked is A.attn_fwd_chunked
+
+
 def test_strerror_covers_every_code():
     seen = set()
     for code in A.STATUS:
@@ -73,7 +88,7 @@ def call(**kw):
     (dict(chunk=0), 6), (dict(kv_len=0), 6), (dict(kv_len=121), 6),
     (dict(S_q=121, kv_len=120), 5), (dict(S_q=50, kv_len=40), 5),
     (dict(q=Q + 8), 7), (dict(o=O + 4), 7), (dict(v=V + 2), 7),
-    (dict(o=Q), 8), (dict(o=K + 1024), 8), (dict(o=V - 16), 8),
+    (dict(o=Q), A.ATTN_E_OVERLAP), (dict(o=K + 1024), A.ATTN_E_OVERLAP), (dict(o=V - 16), A.ATTN_E_OVERLAP),
 ])
 def test_invalid_arguments_return_their_code(kw, code):
     assert call(**kw) == code
@@ -83,8 +98,8 @@ def test_valid_call_without_gpu_reports_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert call() == 9
-    assert A.lib.attn_fwd(Q, K, V, O, 2, 3, 100, 120, 64, 0, 0.125, 0, None) == 9
+    assert call() == A.ATTN_E_DEVICE
+    assert A.lib.attn_fwd(Q, K, V, O, 2, 3, 100, 120, 64, 0, 0.125, 0, None) == A.ATTN_E_DEVICE
 
 
 def test_largest_head_passes_validation():
@@ -94,14 +109,14 @@ def test_largest_head_passes_validation():
         pytest.skip("a GPU is present")
     q, k, v, o = 1 << 40, 1 << 41, 1 << 42, 1 << 43
     for dtype, s_kv in ((0, (1 << 24) - 1), (2, (1 << 25) - 1), (1, (1 << 25) - 1)):
-        assert A.lib.attn_fwd_chunked(q, k, v, o, 1, 1, 100, s_kv, 64, 1, 0.125, dtype, None, 64, s_kv) == 9
+        assert A.lib.attn_fwd_chunked(q, k, v, o, 1, 1, 100, s_kv, 64, 1, 0.125, dtype, None, 64, s_kv) == A.ATTN_E_DEVICE
 
 
 def test_noncausal_allows_more_queries_than_keys():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert call(causal=0, S_q=500, kv_len=7) == 9  # passes validation, stops at the device check
+    assert call(causal=0, S_q=500, kv_len=7) == A.ATTN_E_DEVICE  # passes validation, stops at the device check
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -182,7 +197,7 @@ def call_append(**kw):
     (dict(B=1 << 16, H=1 << 15, S_cap=1 << 30, kv_len=0, n=1), 2),  # byte count overflow
     (dict(dtype=5), 3),
     (dict(kc=KC + 8), 7), (dict(vn=VN + 4), 7),
-    (dict(vc=KC + 4096), 8), (dict(kn=VC + 64), 8), (dict(vn=KC), 8),
+    (dict(vc=KC + 4096), A.ATTN_E_OVERLAP), (dict(kn=VC + 64), A.ATTN_E_OVERLAP), (dict(vn=KC), A.ATTN_E_OVERLAP),
 ])
 def test_append_invalid_arguments_return_their_code(kw, code):
     assert call_append(**kw) == code
@@ -192,8 +207,8 @@ def test_append_valid_call_without_gpu_reports_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert call_append() == 9
-    assert call_append(kv_len=0, n=100, dtype=0) == 9   # fills the whole cache
+    assert call_append() == A.ATTN_E_DEVICE
+    assert call_append(kv_len=0, n=100, dtype=0) == A.ATTN_E_DEVICE   # fills the whole cache
 
 
 # attn_fwd_varlen: per-sequence key lengths in a device array (a fake aligned
@@ -214,7 +229,7 @@ def call_varlen(**kw):
     (dict(B=0), 2), (dict(S_kv=0), 2), (dict(D=128), 2), (dict(B=1 << 20, H=1 << 12), 2),
     (dict(dtype=4), 3), (dict(scale=float("nan")), 4),
     (dict(lens=LENS + 2), 7), (dict(lens=LENS + 1), 7), (dict(k=K + 8), 7),
-    (dict(o=V), 8),
+    (dict(o=V), A.ATTN_E_OVERLAP),
 ])
 def test_varlen_invalid_arguments_return_their_code(kw, code):
     assert call_varlen(**kw) == code
@@ -224,11 +239,11 @@ def test_varlen_valid_call_without_gpu_reports_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert call_varlen() == 9
+    assert call_varlen() == A.ATTN_E_DEVICE
     # A causal call with more query rows than keys passes validation: rows
     # that see no key are defined (zeros), unlike attn_fwd's ATTN_E_CAUSAL.
-    assert call_varlen(S_q=200, S_kv=120) == 9
-    assert call_varlen(lens=LENS + 4, dtype=0, causal=0) == 9   # 4-byte alignment is enough for the lengths
+    assert call_varlen(S_q=200, S_kv=120) == A.ATTN_E_DEVICE
+    assert call_varlen(lens=LENS + 4, dtype=0, causal=0) == A.ATTN_E_DEVICE   # 4-byte alignment is enough for the lengths
 
 
 
@@ -248,7 +263,7 @@ def call_split(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(B=0), 2), (dict(D=32), 2), (dict(dtype=7), 3), (dict(scale=float("inf")), 4),
     (dict(S_q=121, kv_len=120), 5), (dict(kv_len=0), 6), (dict(kv_len=121), 6), (dict(k=K + 2), 7),
-    (dict(o=K), 8),
+    (dict(o=K), A.ATTN_E_OVERLAP),
     (dict(n=0), 11), (dict(n=-3), 11), (dict(n=1025), 11),
     (dict(ws=0), 12), (dict(ws=WS + 8), 12), (dict(ws_bytes=4 * 2 * 3 * 100 * 264 - 1), 12),
     (dict(ws=Q), 12), (dict(ws=V - 1024), 12), (dict(ws=O + 16), 12),
@@ -261,9 +276,9 @@ def test_splitkv_valid_calls_without_gpu_report_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert call_split() == 9
-    assert call_split(n=1, ws=0, ws_bytes=0) == 9        # one range needs no workspace
-    assert call_split(n=1024, ws_bytes=1024 * 2 * 3 * 100 * 264) == 9
+    assert call_split() == A.ATTN_E_DEVICE
+    assert call_split(n=1, ws=0, ws_bytes=0) == A.ATTN_E_DEVICE        # one range needs no workspace
+    assert call_split(n=1024, ws_bytes=1024 * 2 * 3 * 100 * 264) == A.ATTN_E_DEVICE
 
 
 def test_splitkv_workspace_bytes():
@@ -310,7 +325,7 @@ def call_proj(**kw):
     (dict(H=1 << 26), 2),                             # 3d over 2^31
     (dict(dtype=0), 3), (dict(dtype=9), 3),
     (dict(x=PX + 8), 7), (dict(b=PB + 2), 7), (dict(v=PV + 4), 7),
-    (dict(q=PX), 8), (dict(k=PW + 64), 8), (dict(v=PB), 8), (dict(k=PQ + 1024), 8),
+    (dict(q=PX), A.ATTN_E_OVERLAP), (dict(k=PW + 64), A.ATTN_E_OVERLAP), (dict(v=PB), A.ATTN_E_OVERLAP), (dict(k=PQ + 1024), A.ATTN_E_OVERLAP),
 ])
 def test_proj_invalid_arguments_return_their_code(kw, code):
     assert call_proj(**kw) == code
@@ -320,5 +335,5 @@ def test_proj_valid_calls_without_gpu_report_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert call_proj() == 9
-    assert call_proj(b=0, dtype=1) == 9      # no bias, fp16
+    assert call_proj() == A.ATTN_E_DEVICE
+    assert call_proj(b=0, dtype=1) == A.ATTN_E_DEVICE      # no bias, fp16

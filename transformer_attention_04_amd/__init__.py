@@ -5,8 +5,8 @@ kernels behind the C ABI declared in include/attn.h.  torch supplies device
 memory and the current stream.  There is no fallback: if the library is not
 built, importing this package raises.
 
-    attn_fwd(q, k, v, causal=False, scale=None)            -> o
-    attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o
+    attn_fwd(q, k, v, causal=False, scale=None)            -> o   (alias fwd)
+    attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o   (alias fwd_chunked)
     attn_fwd_varlen(q, k, v, kv_lens, causal=False, ...)     -> o
     attn_fwd_splitkv(q, k, v, causal=False, n_split=0, ...)  -> o
     attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len)   -> kv_len + n
@@ -29,9 +29,10 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_DTYPE", 4: "ATTN_E_SCALE",
-    5: "ATTN_E_CAUSAL", 6: "ATTN_E_CHUNK", 7: "ATTN_E_ALIGN", 8: "ATTN_E_OVERLAP",
-    9: "ATTN_E_DEVICE", 10: "ATTN_E_LAUNCH", 11: "ATTN_E_SPLIT", 12: "ATTN_E_WORKSPACE",
+    5: "ATTN_E_CAUSAL", 6: "ATTN_E_CHUNK", 7: "ATTN_E_ALIGN", 8: "ATTN_E_DEVICE",
+    9: "ATTN_E_HIP", 10: "ATTN_E_OVERLAP", 11: "ATTN_E_SPLIT", 12: "ATTN_E_WORKSPACE",
 }
+globals().update({name: code for code, name in STATUS.items()})
 EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
            "attn_splitkv_choose", "attn_kv_append", "attn_qkv_proj", "attn_strerror", "attn_sched_grid",
            "attn_sched_tile")
@@ -322,6 +323,12 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o
+
+
+# The short names of the binding: attn.fwd(q, k, v, causal=..., scale=None)
+# and attn.fwd_chunked(..., chunk, kv_len) are the two entry points above.
+fwd = attn_fwd
+fwd_chunked = attn_fwd_chunked
 
 
 def sched_grid(B: int, H: int, S_q: int, chunk: int, kv_len: int | None = None, causal: bool = True) -> int:

@@ -1136,11 +1136,11 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
     else
       hipLaunchKernelGGL((attn_fwd_kernel<T, false, 1, false, true>), dim3(grid * n_split), dim3(NTHREADS), 0,
                          stream, p);
-    if (hipGetLastError() != hipSuccess) return ATTN_E_LAUNCH;
+    if (hipGetLastError() != hipSuccess) return ATTN_E_HIP;
     const int64_t mblocks = (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS;
     hipLaunchKernelGGL((splitkv_merge_kernel<T>), dim3((unsigned)mblocks), dim3(MERGE_THREADS), 0, stream,
                        p.ws_acc, p.ws_ml, static_cast<T*>(o), rows, n_split);
-    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
   }
   // Few 128-row query tiles (at most two per CU): split each tile's key range
   // between two wave groups so every SIMD runs two waves on half the key
@@ -1151,7 +1151,7 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
     launch_kernel<T, 2>(p, grid, causal, stream);
   else
     launch_kernel<T, 1>(p, grid, causal, stream);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 // ---------------------------------------------------------------------------
@@ -1213,7 +1213,7 @@ extern "C" int attn_kv_append(void* k_cache, void* v_cache, const void* k_new, c
                      static_cast<hipStream_t>(stream), static_cast<char*>(k_cache), static_cast<char*>(v_cache),
                      static_cast<const char*>(k_new), static_cast<const char*>(v_new), bh, head_units,
                      (int64_t)S_cap * row_bytes, (int64_t)kv_len * row_bytes);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 extern "C" int attn_fwd_chunked(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
@@ -1361,7 +1361,7 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_E_ALIGN: return "tensor base pointer not 16-byte aligned";
     case ATTN_E_OVERLAP: return "output overlaps an input";
     case ATTN_E_DEVICE: return "current HIP device missing or not gfx950";
-    case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_HIP: return "HIP runtime error at kernel launch";
     case ATTN_E_SPLIT: return "n_split outside [1, 1024], or the split grid is too large";
     case ATTN_E_WORKSPACE: return "workspace null, not 16-byte aligned, too small, or overlapping a tensor";
     default: return "unknown attn status";

@@ -216,7 +216,7 @@ int launch_proj(const void* x, const void* w, const void* bias, void* q, void* k
   p.tiles_n = (p.N + PN - 1) / PN;
   p.tiles = ((p.M + PM - 1) / PM) * p.tiles_n;
   hipLaunchKernelGGL((qkv_proj_kernel<T>), dim3(p.tiles), dim3(PTHREADS), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 }  // namespace
