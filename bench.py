@@ -4,15 +4,20 @@
 One step = one attn_fwd (or attn_fwd_chunked) call over one set of synthetic
 inputs already resident in HBM.  Inputs rotate over enough sets that the timed
 footprint exceeds the 256 MB Infinity Cache, so short workloads measure HBM,
-not the cache.  Prints ONE JSON line (rank 0, N = 1):
+not the cache; the set index runs on across repeats, so every set is timed.
+Prints ONE JSON line (rank 0, N = 1):
 
   value        counted TFLOP/s = 4*B*H*S_q*S_kv*D (halved when causal) / time
   ms_per_step  mean time per call over the timed region (HIP events)
   roofline     the kernel against its binding MI355X peak (MFMA or HBM)
   cpu_baseline the fp64 oracle on a bounded sample of the same workload, on
                this host's cores
+  per_config   the other workloads (c1 .. c4, every dtype), each with its own
+               ms/call, TFLOP/s, roofline and cpu_baseline
 
-Default workload: multi-head non-causal S=512 (B=8, H=8, D=64) in fp32.
+Default workload: the long-context causal chunked workload (B=16, H=16,
+S=98,304, D=64, bf16, 4,096-row query windows against the K/V cache), the
+largest of the five workloads; --workload NAME times one other workload alone.
 """
 from __future__ import annotations
 
@@ -34,6 +39,10 @@ PEAK = {  # MI355X datasheet, dense
     "hbm": 8000.0,  # GB/s
 }
 ROTATE_BYTES = 1 << 30  # timed footprint target (> 256 MB Infinity Cache)
+HEADLINE = "c5_long_causal_chunked"
+# The other workloads, every dtype: reported under per_config.
+PER_CONFIG = [("c1_single_head_f32", "f32"), ("c2_mha_s512", "f32"), ("c2_mha_s512", "f16"),
+              ("c3_causal_s2048", "bf16"), ("c3_causal_s2048", "f16"), ("c4_large_batch_s1024", "bf16")]
 
 
 def log(*a):
@@ -49,7 +58,15 @@ def parse():
     ap.add_argument("--repeats", type=int, default=5,
                     help="the timed steps are split into this many back-to-back repeats (median reported)")
     ap.add_argument("--no-aa", action="store_true", help="skip the A/A control (a second timing of the same steps)")
-    ap.add_argument("--workload", default="c2_mha_s512")
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="the workload of the headline line (default: the long-context chunked workload); "
+                         "the per-config block is added only for the default")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time the headline workload alone (no per_config block)")
+    ap.add_argument("--per-config-seconds", type=float, default=0.25,
+                    help="GPU time per per-config entry (its step count follows from a short estimate)")
+    ap.add_argument("--per-config-cpu-seconds", type=float, default=3.0,
+                    help="oracle time per per-config entry's cpu_baseline")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -323,6 +340,78 @@ def split_steps(k, r):
     return [k // r + (1 if i < k % r else 0) for i in range(r)]
 
 
+def repeat_bases(sizes):
+    """First global step index of each repeat: the input-set index runs on
+    from one repeat to the next, so k steps touch min(k, n_sets) sets."""
+    out, b = [], 0
+    for n in sizes:
+        out.append(b)
+        b += n
+    return out
+
+
+def sets_timed(k, n_sets):
+    """Distinct input sets that k steps over n_sets rotating sets touch."""
+    return min(k, n_sets)
+
+
+class Timer:
+    """Exactly `steps` steps in back-to-back repeats, timed with HIP events on
+    the launch stream.  Repeat r runs global steps base_r .. base_r + n_r - 1
+    (step(i) picks input set i mod n_sets), captured once into a HIP graph and
+    replayed (eager: launched from Python), so the timed region holds exactly
+    the steps' kernels."""
+
+    def __init__(self, step, steps, repeats, eager, stream, replay_once=True):
+        import torch
+        self.stream = stream
+        self.sizes = split_steps(steps, repeats)
+        self.bases = repeat_bases(self.sizes)
+        self.step = step
+        self.graphs = []
+        if not eager:
+            for b, n in zip(self.bases, self.sizes):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(b, b + n):
+                        step(i)
+                if replay_once:
+                    g.replay()  # one untimed replay
+                self.graphs.append(g)
+            torch.cuda.synchronize()
+
+    @property
+    def launch(self):
+        return "hip_graph_replay" if self.graphs else "eager"
+
+    def run(self):
+        """Returns (total ms, [ms per step of each repeat])."""
+        import torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(self.sizes) + 1)]
+        ev[0].record(self.stream)
+        for r, (b, n) in enumerate(zip(self.bases, self.sizes)):
+            if self.graphs:
+                self.graphs[r].replay()
+            else:
+                for i in range(b, b + n):
+                    self.step(i)
+            ev[r + 1].record(self.stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[-1]), [ev[r].elapsed_time(ev[r + 1]) / n for r, n in enumerate(self.sizes)]
+
+
+def estimate_ms(step, stream, n):
+    """Mean eager ms per step over n steps (after the warmup)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def bench_qkv(args, w, dtype):
     """Time attn_qkv_proj on the workload's batch, sequence and heads."""
     import torch
@@ -355,38 +444,13 @@ def bench_qkv(args, w, dtype):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     if args.steps is None:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(10):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        args.steps = int(min(20000, max(10, math.ceil(500.0 / max(e0.elapsed_time(e1) / 10, 1e-3)))))
-    sizes = split_steps(args.steps, args.repeats)
-    graphs = {}
-    if not args.eager:
-        for n in sorted(set(sizes)):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                for i in range(n):
-                    step(i)
-            gr.replay()
-            graphs[n] = gr
-        torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
+        est = estimate_ms(step, stream, 10)
+        args.steps = int(min(20000, max(10, math.ceil(500.0 / max(est, 1e-3)))))
+    tm = Timer(step, args.steps, args.repeats, args.eager, stream)
     clk0 = gpu_clock_mhz(dev)
-    ev[0].record(stream)
-    for r, n in enumerate(sizes):
-        if graphs:
-            graphs[n].replay()
-        else:
-            for i in range(n):
-                step(i)
-        ev[r + 1].record(stream)
-    torch.cuda.synchronize()
+    total_ms, rep_ms = tm.run()
     clk1 = gpu_clock_mhz(dev)
-    ms = ev[0].elapsed_time(ev[-1]) / args.steps
-    rep_ms = [ev[r].elapsed_time(ev[r + 1]) / n for r, n in enumerate(sizes)]
+    ms = total_ms / args.steps
     sec = ms / 1e3
     tflops = flops / sec / 1e12
     pk = PEAK[f"mfma_{dtype}"]
@@ -396,12 +460,13 @@ def bench_qkv(args, w, dtype):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}_qkv_projection", "B": B, "S": S, "H": H, "d": d, "bias": True,
-                   "rotating_sets": n_sets, "mode": "attn_qkv_proj: x [B,S,d] @ W^T [d,3d] + b -> q,k,v [B,H,S,64]",
-                   "launch": "hip_graph_replay" if graphs else "eager"},
+                   "rotating_sets": n_sets, "sets_timed": sets_timed(args.steps, n_sets),
+                   "mode": "attn_qkv_proj: x [B,S,d] @ W^T [d,3d] + b -> q,k,v [B,H,S,64]",
+                   "launch": tm.launch},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": pk, "unit": "TFLOP/s",
                      "frac": round(tflops / pk, 4), "traffic": None,
                      "algorithmic_bytes": nbytes, "peak_source": "datasheet"},
-        "timing": {"repeats": len(rep_ms), "steps_per_repeat": sizes,
+        "timing": {"repeats": len(rep_ms), "steps_per_repeat": tm.sizes,
                    "ms_per_step_each_repeat": [round(x, 6) for x in rep_ms],
                    "median_ms_per_step": round(sorted(rep_ms)[len(rep_ms) // 2], 6),
                    "gpu_clock_mhz": {"before": clk0, "after": clk1}},
@@ -412,11 +477,119 @@ def bench_qkv(args, w, dtype):
     if mp is not None:
         mp["frac"] = round(tflops / mp["peak"], 4)
     line["roofline"]["measured"] = mp
+    emit(args, line)
+
+
+def emit(args, line):
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
         with open(args.out, "a") as f:
             f.write(s + "\n")
+
+
+def clock_block(clk0, clk1):
+    return {"before": clk0, "after": clk1,
+            "after_over_before": round(clk1 / clk0, 4) if clk0 and clk1 else None,
+            "below_85pct": (clk1 < 0.85 * clk0) if clk0 and clk1 else None}
+
+
+def make_sets(w, dtype, dev, log_name=True):
+    """The rotating input sets of a workload: distinct buffers holding the same
+    seeded values, enough of them (at most 64, within 90% of the free device
+    memory) that their footprint exceeds the Infinity Cache.  Large workloads
+    are drawn on the device (one set).  Exits with status 3 when one set does
+    not fit."""
+    import torch
+    import workloads as W
+    footprint = w.bytes(dtype)
+    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
+    free_b, _ = torch.cuda.mem_get_info(dev)
+    if footprint > 0.9 * free_b:
+        print(f"bench.py: workload {w.name} needs {footprint / 2**30:.1f} GiB of device memory, "
+              f"{free_b / 2**30:.1f} GiB are free", file=sys.stderr)
+        sys.exit(3)
+    n_sets = max(1, min(n_sets, int(0.9 * free_b // footprint)))
+    sets = []
+    if w.S_q * w.S_kv * w.B * w.H > (1 << 32) or w.B * w.H * w.S_kv * w.D > (1 << 28):  # large: draw on the device
+        q, k, v = W.make_device_inputs(w, dtype, dev)
+        sets.append((q, k, v, torch.empty_like(q)))
+    else:
+        q0, k0, v0 = (x.to(dev) for x in W.make_inputs(w, dtype))
+        for i in range(n_sets):
+            if i == 0:
+                q, k, v = q0, k0, v0
+            else:  # distinct buffers, same values: the cache cannot hold them all
+                q, k, v = q0.clone(), k0.clone(), v0.clone()
+            sets.append((q, k, v, torch.empty_like(q)))
+    if log_name:
+        log(f"[bench] workload {w.name} dtype {dtype}: {footprint / 1e6:.1f} MB per set, {len(sets)} sets")
+    return sets
+
+
+def per_config_entry(args, name, dtype, dev, stream, peaks):
+    """One per-config result: the workload's single call (attn_fwd, or
+    attn_fwd_chunked for a chunked workload) over rotating sets, timed like the
+    headline but for about --per-config-seconds of GPU time."""
+    import torch
+    import workloads as W
+    import transformer_attention_04_amd as A
+    w = W.BY_NAME[name]
+    sets = make_sets(w, dtype, dev)
+
+    def step(i):
+        q, k, v, o = sets[i % len(sets)]
+        if w.chunk:
+            A.attn_fwd_chunked(q, k, v, chunk=w.chunk, causal=w.causal, scale=w.scale, out=o)
+        else:
+            A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o)
+
+    for i in range(20):
+        step(i)
+    torch.cuda.synchronize()
+    est = estimate_ms(step, stream, 20)
+    steps = int(min(20000, max(len(sets), math.ceil(args.per_config_seconds * 1e3 / max(est, 1e-3)))))
+    tm = Timer(step, steps, args.repeats, args.eager, stream)
+    clk0 = gpu_clock_mhz(dev)
+    total_ms, rep_ms = tm.run()
+    clk1 = gpu_clock_mhz(dev)
+    ms = total_ms / steps
+    sec = ms / 1e3
+    tflops = w.flops() / sec / 1e12
+    roof = roofline_for(w, dtype, sec)
+    roof["traffic"] = measured_traffic(w.name, dtype)
+    roof["peak_source"] = "datasheet"
+    key = (roof["bound"], dtype if roof["bound"] == "mfma" else "hbm")
+    if key not in peaks:
+        peaks[key] = measured_peak(dev, roof["bound"], dtype)
+    mp = dict(peaks[key]) if peaks[key] else None
+    if mp is not None:
+        mp["frac"] = round(roof["achieved"] / mp["peak"], 4)
+    roof["measured"] = mp
+    med = sorted(rep_ms)[len(rep_ms) // 2]
+    log(f"[bench] per-config {name} {dtype}: {ms * 1e3:.2f} us/call, {tflops:.2f} TFLOP/s, "
+        f"{roof['bound']} frac {roof['frac']}")
+    e = torch.finfo(W.DTYPES[dtype]).bits // 8
+    entry = {
+        "workload": name, "dtype": dtype, "ms_per_call": round(ms, 6), "median_ms_per_call": round(med, 6),
+        "tflops": round(tflops, 4), "steps": steps, "rotating_sets": len(sets),
+        "sets_timed": sets_timed(steps, len(sets)), "launch": tm.launch,
+        "shape": {"B": w.B, "H": w.H, "S_q": w.S_q, "S_kv": w.S_kv, "D_h": w.D, "causal": w.causal,
+                  "chunk": w.chunk},
+        "roofline": roof,
+        "bandwidth": {"algorithmic_bytes": int(w.bytes(dtype)), "gbps": round(w.bytes(dtype) / sec / 1e9, 2)},
+        "timing": {"repeats": len(rep_ms), "steps_per_repeat": tm.sizes,
+                   "ms_per_step_each_repeat": [round(x, 6) for x in rep_ms],
+                   "gpu_clock_mhz": clock_block(clk0, clk1)},
+    }
+    assert e in (2, 4)
+    del tm, sets
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        entry["cpu_baseline"] = cpu_baseline(w, dtype, args.per_config_cpu_seconds)
+    else:
+        entry["cpu_baseline"] = None
+    return entry
 
 
 def main():
@@ -439,6 +612,8 @@ def main():
             print("--qkv takes a 16-bit dtype and neither --varlen, --stream nor --decode", file=sys.stderr)
             sys.exit(2)
         return bench_qkv(args, w, dtype)
+    special = bool(args.decode or args.varlen or args.stream)
+    with_per_config = not args.no_per_config and not special and args.workload == HEADLINE and args.dtype is None
     if args.decode:
         if args.varlen or args.stream:
             print("--decode takes neither --varlen nor --stream", file=sys.stderr)
@@ -448,27 +623,7 @@ def main():
                                 sample_rows=None)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    footprint = w.bytes(dtype)
-    n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / footprint)))
-    free_b, _ = torch.cuda.mem_get_info(dev)
-    if footprint > 0.9 * free_b:  # inputs and output of one set (plus the decode workspace, which is small)
-        print(f"bench.py: workload {w.name} needs {footprint / 2**30:.1f} GiB of device memory, "
-              f"{free_b / 2**30:.1f} GiB are free", file=sys.stderr)
-        sys.exit(3)
-    n_sets = max(1, min(n_sets, int(0.9 * free_b // footprint)))
-    log(f"[bench] workload {w.name} dtype {dtype}: {footprint / 1e6:.1f} MB per set, {n_sets} sets")
-    sets = []
-    if w.S_q * w.S_kv * w.B * w.H > (1 << 32) or w.B * w.H * w.S_kv * w.D > (1 << 28):  # large: draw on the device
-        q, k, v = W.make_device_inputs(w, dtype, dev)
-        sets.append((q, k, v, torch.empty_like(q)))
-    else:
-        q0, k0, v0 = (x.to(dev) for x in W.make_inputs(w, dtype))
-        for i in range(n_sets):
-            if i == 0:
-                q, k, v = q0, k0, v0
-            else:  # distinct buffers, same values: the cache cannot hold them all
-                q, k, v = q0.clone(), k0.clone(), v0.clone()
-            sets.append((q, k, v, torch.empty_like(q)))
+    sets = make_sets(w, dtype, dev)
     chunk = w.chunk
     work = None
     if args.decode:
@@ -502,6 +657,7 @@ def main():
         vc = torch.full_like(v, float("nan"))
         del sets[:], q, k, v, o
         log(f"[bench] streaming: {len(bounds)} windows of {chunk} rows")
+    n_sets = 1 if args.stream else len(sets)
 
     def step(i):
         if args.stream:
@@ -524,53 +680,19 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    if args.steps is None:  # about 0.5 s of GPU time, from a short eager estimate
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n_est = 3 if args.stream or chunk else 20
-        e0.record(stream)
-        for i in range(n_est):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        est = e0.elapsed_time(e1) / n_est
+    long_steps = bool(args.stream or chunk)
+    if args.steps is None:  # about 0.5 s of GPU time (long workloads: 10 steps), from a short eager estimate
+        est = estimate_ms(step, stream, 3 if long_steps else 20)
         args.steps = int(min(20000, max(10, math.ceil(500.0 / max(est, 1e-3)))))
-        if args.stream or chunk:
-            args.steps = min(args.steps, 5)
+        if long_steps:
+            args.steps = min(args.steps, 10)
         log(f"[bench] ~{est * 1e3:.1f} us per eager step: timing {args.steps} steps")
-    sizes = split_steps(args.steps, args.repeats)
-    graphs = {}
-    if not args.eager:
-        # The timed steps are captured into HIP graphs (one per repeat size)
-        # and replayed, so host-side call overhead does not leave the GPU idle
-        # between the short kernels.  The kernels and their inputs are the
-        # same as in eager mode.
-        for n in sorted(set(sizes)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(n):
-                    step(i)
-            g.replay()  # one untimed replay
-            graphs[n] = g
-        torch.cuda.synchronize()
-
-    def timed():
-        """Exactly args.steps steps, in back-to-back repeats, between HIP events
-        on the launch stream.  Returns (total ms, [ms per step of each repeat])."""
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
-        ev[0].record(stream)
-        for r, n in enumerate(sizes):
-            if graphs:
-                graphs[n].replay()
-            else:
-                for i in range(n):
-                    step(i)
-            ev[r + 1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[-1]), [ev[r].elapsed_time(ev[r + 1]) / n for r, n in enumerate(sizes)]
+    # Steps of ~0.3 s need no untimed replay of each graph before the timing.
+    tm = Timer(step, args.steps, args.repeats, args.eager, stream, replay_once=not long_steps)
 
     clk0 = gpu_clock_mhz(dev)
     t0 = time.perf_counter()
-    total_ms, rep_ms = timed()
+    total_ms, rep_ms = tm.run()
     wall = time.perf_counter() - t0
     clk1 = gpu_clock_mhz(dev)
     ms = total_ms / args.steps
@@ -581,7 +703,7 @@ def main():
         f"{tflops:.2f} TFLOP/s, wall {wall:.3f} s, clock {clk0} -> {clk1} MHz")
     aa = None
     if not args.no_aa:  # A/A control: the same steps timed again in this process
-        total2, _ = timed()
+        total2, _ = tm.run()
         aa = round(total2 / total_ms, 4)
         log(f"[bench] A/A: second timing / first = {aa}")
 
@@ -591,20 +713,21 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_q": w.S_q, "S_kv": w.S_kv, "D_h": w.D,
-                   "causal": w.causal, "chunk": w.chunk, "rotating_sets": 1 if args.stream else len(sets),
+                   "causal": w.causal, "chunk": w.chunk, "rotating_sets": n_sets,
+                   "sets_timed": sets_timed(args.steps, n_sets),
                    "mode": (f"decode: {w.S_q} query row(s) against the whole cache, keys split over "
                             f"{n_split} workgroup range(s) (attn_fwd_splitkv)" if args.decode else
                             "stream: append + attend per window" if args.stream else
                             "varlen: per-sequence key lengths uniform on [S_kv/4, S_kv], visible pairs counted"
-                            if args.varlen else "single call"),
-                   "launch": "hip_graph_replay" if graphs else "eager"},
+                            if args.varlen else
+                            f"single attn_fwd_chunked call, {-(-w.S_q // chunk)} windows of {chunk} query rows"
+                            if chunk else "single attn_fwd call"),
+                   "launch": tm.launch},
         "roofline": roofline_for(w, dtype, sec, work),
-        "timing": {"repeats": len(rep_ms), "steps_per_repeat": sizes,
+        "timing": {"repeats": len(rep_ms), "steps_per_repeat": tm.sizes,
                    "ms_per_step_each_repeat": [round(x, 6) for x in rep_ms],
                    "median_ms_per_step": round(med, 6),
-                   "gpu_clock_mhz": {"before": clk0, "after": clk1,
-                                     "after_over_before": round(clk1 / clk0, 4) if clk0 and clk1 else None,
-                                     "below_85pct": (clk1 < 0.85 * clk0) if clk0 and clk1 else None},
+                   "gpu_clock_mhz": clock_block(clk0, clk1),
                    "aa_ratio": aa},
         "environment": environment(dev),
     }
@@ -613,25 +736,32 @@ def main():
                          "note": "Q, K, V read once and O written once per call, over the measured time"}
     if args.varlen:
         line["config"]["kv_lens"] = lens_cpu.tolist()
-    line["roofline"]["traffic"] = (None if (args.stream or args.varlen or args.decode)
-                                   else measured_traffic(w.name, dtype))
+    line["roofline"]["traffic"] = None if special else measured_traffic(w.name, dtype)
     # The datasheet peak is the headline; the ceiling measured on this machine is
     # reported beside it, labelled.
-    mp = measured_peak(dev, line["roofline"]["bound"], dtype)
+    peaks = {}
+    bound = line["roofline"]["bound"]
+    peaks[(bound, dtype if bound == "mfma" else "hbm")] = mp = measured_peak(dev, bound, dtype)
+    mp = dict(mp) if mp else None
     if mp is not None:
         mp["frac"] = round(line["roofline"]["achieved"] / mp["peak"], 4)
     line["roofline"]["peak_source"] = "datasheet"
     line["roofline"]["measured"] = mp
+    del tm, sets
+    if args.stream:
+        del win, kc, vc
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_sample_seconds)
     else:
         line["cpu_baseline"] = None
-    s = json.dumps(line)
-    print(s, flush=True)
-    if args.out:
-        with open(args.out, "a") as f:
-            f.write(s + "\n")
+    if with_per_config:
+        line["per_config"] = [per_config_entry(args, name, dt, dev, stream, peaks) for name, dt in PER_CONFIG]
+        line["per_config_note"] = ("each entry times its workload alone for about --per-config-seconds of GPU "
+                                   "time (its own step count, 5 repeats, graph replay, rotating sets), "
+                                   "independent of --steps and --warmup, which set the headline's steps")
+    emit(args, line)
 
 
 if __name__ == "__main__":

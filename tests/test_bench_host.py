@@ -83,3 +83,27 @@ def test_multi_gpu_request_exits_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_repeats_carry_the_set_index_so_every_set_is_timed():
+    # 20 steps in 5 repeats over 32 rotating sets: the repeats cover global
+    # steps 0..19 (not 0..3 five times), so 20 distinct sets are timed.
+    for k, r, n_sets in ((20, 5, 32), (7, 5, 3), (100, 5, 64), (3, 5, 1), (12500, 5, 32)):
+        sizes = bench.split_steps(k, r)
+        bases = bench.repeat_bases(sizes)
+        idx = [i for b, n in zip(bases, sizes) for i in range(b, b + n)]
+        assert idx == list(range(k))
+        touched = {i % n_sets for i in idx}
+        assert len(touched) == bench.sets_timed(k, n_sets) == min(k, n_sets)
+
+
+def test_default_line_is_the_long_context_workload_with_per_config():
+    assert bench.HEADLINE == "c5_long_causal_chunked"
+    w = W.BY_NAME[bench.HEADLINE]
+    assert (w.B, w.H, w.S_q, w.S_kv, w.D, w.causal, w.chunk, w.dtypes[0]) == (16, 16, 98304, 98304, 64, True,
+                                                                            4096, "bf16")
+    names = {(n, d) for n, d in bench.PER_CONFIG}
+    for wl in W.WORKLOADS:
+        if wl.name != bench.HEADLINE:
+            for d in wl.dtypes:
+                assert (wl.name, d) in names

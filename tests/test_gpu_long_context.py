@@ -68,3 +68,21 @@ def test_long_context_chunked_equals_single_window(long_run):
     o2 = A.attn_fwd(q, k, v, causal=True, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
+
+
+@pytest.mark.timeout(300)
+def test_long_context_streaming_windows_equal_single_call(long_run):
+    """A streaming caller -- one attn_fwd_chunked call per 4,096-row window,
+    each with S_q = 4,096 and the cache grown to the window's end (24 calls)
+    -- gets the single chunked call's output bit for bit."""
+    import transformer_attention_04_amd as A
+    w, q, k, v, o = long_run
+    out = torch.empty_like(q)
+    for start in range(0, w.S_q, w.chunk):
+        stop = min(w.S_q, start + w.chunk)
+        qw = q[:, :, start:stop].contiguous()
+        out[:, :, start:stop] = A.attn_fwd_chunked(qw, k, v, chunk=w.chunk, kv_len=stop, causal=True,
+                                                   scale=w.scale)
+    torch.cuda.synchronize()
+    say(f"[long] {-(-w.S_q // w.chunk)} streaming calls done")
+    assert torch.equal(out, o)

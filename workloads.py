@@ -164,3 +164,59 @@ def varlen_lengths(B: int, S_kv: int, seed: int, low: float = 0.25, edges: bool 
             if i < B:
                 lens[i] = L
     return lens.to(torch.int32)
+
+
+# Scale at which a score is exactly q.k in log2 units for the kernels
+# (|scale| * log2 e rounds to 1.0 in fp32): float32(ln 2).
+LN2_F32 = float(torch.tensor(0.6931471805599453, dtype=torch.float32))
+
+
+def rescale_levels(S_kv: int, D: int = 64, steady: int = 8, jump: int = 17) -> torch.Tensor:
+    """[S_kv, D] float32 integer key levels for the forced-rescale inputs.
+
+    Keys come in pairs of 64-key tiles (128 keys).  Column d walks its own
+    schedule with a running level m (start 0): pair 0 holds every key at 0;
+    afterwards pairs cycle, with phase d % 3, through two "steady" pairs, every
+    key at m + steady, and one "jump" pair, every key at m except one per
+    64-key tile (offset (5d + 3) % 64) at m + jump, after which m grows by
+    jump.  Past column d's last pair, 1 + (7d) % n_pairs, every key sits at
+    m - 40 (weight 2^-40, nothing).  With one-hot queries and scale LN2_F32 the
+    score of a key is its level, exactly, in log2 units."""
+    n_pairs = (S_kv + 127) // 128
+    lev = torch.empty((S_kv, D), dtype=torch.float32)
+    for d in range(D):
+        m, last, off = 0.0, 1 + (7 * d) % max(1, n_pairs), (5 * d + 3) % 64
+        for p in range(n_pairs):
+            a, b = 128 * p, min(S_kv, 128 * p + 128)
+            if p == 0:
+                lev[a:b, d] = 0.0
+            elif p > last:
+                lev[a:b, d] = m - 40.0
+            elif (p - 1 + d % 3) % 3 < 2:
+                lev[a:b, d] = m + steady
+            else:
+                lev[a:b, d] = m
+                for t0 in (a, a + 64):
+                    if t0 + off < b:
+                        lev[t0 + off, d] = m + jump
+                m += jump
+    return lev
+
+
+def rescale_inputs(B: int, H: int, S_q: int, S_kv: int, seed: int, D: int = 64):
+    """(q, k, v) float32 CPU tensors that force the online-softmax offset to be
+    raised while the accumulator holds a large share of the row's weight:
+    query row i of head (b, h) is the unit vector of column (3i + 7(bH + h) + b)
+    % D, every head's keys are rescale_levels, values are N(0, 1) from the
+    seed.  Every level is an integer below 256, exact in bf16, fp16 and fp32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    lev = rescale_levels(S_kv, D)
+    k = lev.expand(B, H, S_kv, D).contiguous()
+    q = torch.zeros((B, H, S_q, D), dtype=torch.float32)
+    for b in range(B):
+        for h in range(H):
+            cols = (3 * torch.arange(S_q) + 7 * (b * H + h) + b) % D
+            q[b, h, torch.arange(S_q), cols] = 1.0
+    v = torch.randn((B, H, S_kv, D), generator=g, dtype=torch.float32)
+    return q, k, v
