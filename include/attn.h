@@ -180,6 +180,34 @@ int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
                      int causal, float scale, int dtype, void *stream,
                      int kv_len, int n_split, void *workspace, size_t workspace_bytes);
 
+/* Size of the device array that attn_fwd_splitkv_noalloc keeps its partial
+ * states in: 16 MiB per GPU. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv for callers that cannot
+ * allocate device memory (code under stream capture into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation).  The partial states
+ * live in a device array the library holds instead of a caller workspace;
+ * the caller still passes q, k, v and o.  Nothing is allocated or freed.
+ *   Arguments as attn_fwd_splitkv without the workspace.  The states take
+ *   attn_splitkv_workspace_bytes(B, H, S_q, n_split) bytes, at most
+ *   ATTN_NOALLOC_SCRATCH_BYTES (16 MiB: for example n_split = 8 ranges of
+ *   7,943 query rows); n_split = 1 needs none.
+ * The array is the library's, one per GPU, from the first call on that GPU
+ * (which looks up its address) until the process ends.  Every call on a GPU
+ * uses the same array: calls that overlap in time on one GPU (two streams,
+ * two threads) race and must not be issued; calls one after another on a
+ * stream are fine.  The result is bit-identical to attn_fwd_splitkv with the
+ * same n_split.  Errors: as attn_fwd_splitkv; ATTN_E_WORKSPACE when the
+ * states would exceed ATTN_NOALLOC_SCRATCH_BYTES (checked before any HIP
+ * call); ATTN_E_HIP if the array's address cannot be looked up.
+ */
+int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o,
+                             int B, int H, int S_q, int S_kv, int D_h,
+                             int causal, float scale, int dtype, void *stream,
+                             int kv_len, int n_split);
+
 /* Workspace bytes attn_fwd_splitkv needs (0 for n_split = 1): n_split * B*H*S_q
  * * 264.  Host only.  ATTN_E_SHAPE for sizes < 1 or an overflow, ATTN_E_SPLIT
  * for n_split out of range. */

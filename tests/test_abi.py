@@ -337,3 +337,22 @@ def test_proj_valid_calls_without_gpu_report_device():
         pytest.skip("a GPU is present")
     assert call_proj() == A.ATTN_E_DEVICE
     assert call_proj(b=0, dtype=1) == A.ATTN_E_DEVICE      # no bias, fp16
+
+
+def test_noalloc_split_checks_before_any_hip_call():
+    """attn_fwd_splitkv_noalloc: the argument checks of attn_fwd_splitkv, and
+    states beyond the library's 16 MiB array are rejected before any HIP call."""
+    import torch
+    f = A.lib.attn_fwd_splitkv_noalloc
+    assert A.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert f(0, K, V, O, 2, 3, 100, 120, 64, 1, 0.125, 2, None, 120, 2) == A.ATTN_E_NULL
+    assert f(Q, K, V, O, 2, 3, 100, 120, 64, 1, 0.125, 2, None, 120, 0) == A.ATTN_E_SPLIT
+    assert f(Q, K, V, Q, 2, 3, 100, 120, 64, 1, 0.125, 2, None, 120, 2) == A.ATTN_E_OVERLAP
+    # 8 ranges x B*H*S_q rows x 264 bytes: 7943 rows fit in 16 MiB, 7944 do not
+    assert A.splitkv_workspace_bytes(1, 1, 7943, 8) <= A.NOALLOC_SCRATCH_BYTES < \
+        A.splitkv_workspace_bytes(1, 1, 7944, 8)
+    big = (1 << 40, 1 << 41, 1 << 42, 1 << 43)
+    assert f(*big, 1, 1, 7944, 9000, 64, 1, 0.125, 2, None, 9000, 8) == A.ATTN_E_WORKSPACE
+    if not torch.cuda.is_available():
+        assert f(*big, 1, 1, 7943, 9000, 64, 1, 0.125, 2, None, 9000, 8) == A.ATTN_E_DEVICE
+        assert f(Q, K, V, O, 2, 3, 100, 120, 64, 1, 0.125, 2, None, 120, 1) == A.ATTN_E_DEVICE

@@ -9,6 +9,7 @@ built, importing this package raises.
     attn_fwd_chunked(q, k, v, chunk, kv_len=None, ...)       -> o   (alias fwd_chunked)
     attn_fwd_varlen(q, k, v, kv_lens, causal=False, ...)     -> o
     attn_fwd_splitkv(q, k, v, causal=False, n_split=0, ...)  -> o
+    attn_fwd_splitkv_noalloc(q, k, v, out, causal=False, ...) -> out
     attn_kv_append(k_cache, v_cache, k_new, v_new, kv_len)   -> kv_len + n
     attn_qkv_proj(x, w, bias=None)                           -> (q, k, v)
     attn_strerror(status)                                    -> str
@@ -33,7 +34,9 @@ STATUS = {
     9: "ATTN_E_HIP", 10: "ATTN_E_OVERLAP", 11: "ATTN_E_SPLIT", 12: "ATTN_E_WORKSPACE",
 }
 globals().update({name: code for code, name in STATUS.items()})
-EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
+NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
+EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc",
+           "attn_splitkv_workspace_bytes",
            "attn_splitkv_choose", "attn_kv_append", "attn_qkv_proj", "attn_strerror", "attn_sched_grid",
            "attn_sched_tile")
 
@@ -68,6 +71,8 @@ def _load(path: str = LIB_PATH):
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, i, i, vp,
                                      ctypes.c_size_t]
     lib.attn_fwd_splitkv.restype = i
+    lib.attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, i, vp, i, i]
+    lib.attn_fwd_splitkv_noalloc.restype = i
     lib.attn_splitkv_workspace_bytes.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_splitkv_workspace_bytes.restype = i
     lib.attn_splitkv_choose.argtypes = [i, i, i, i, i, ctypes.POINTER(i)]
@@ -244,6 +249,34 @@ def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, 
     st = _call(lib.attn_fwd_splitkv, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                B, H, S_q, S_kv, D, int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(dev, stream),
                int(kv_len), int(n_split), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return o
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, out, causal: bool = False, scale: float | None = None,
+                             kv_len: int | None = None, n_split: int = 0, stream=None):
+    """attn_fwd_splitkv with the partial states in the library's own device
+    array (see attn_fwd_splitkv_noalloc in include/attn.h): neither the library
+    nor this wrapper allocates, so `out` (a contiguous tensor like q) is
+    required.  n_split=0 asks attn_splitkv_choose for this GPU's CU count.
+    Calls that overlap in time on one GPU must not be issued (they share the
+    array)."""
+    torch = _t()
+    B, H, S_q, S_kv, D = _check(q, k, v)
+    if kv_len is None:
+        kv_len = S_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if n_split == 0:
+        n_split = splitkv_choose(B, H, S_q, kv_len, torch.cuda.get_device_properties(dev).multi_processor_count)
+    o = out
+    if o is None or o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    st = _call(lib.attn_fwd_splitkv_noalloc, dev, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+               B, H, S_q, S_kv, D, int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(dev, stream),
+               int(kv_len), int(n_split))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return o

@@ -49,6 +49,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "attn.h"
@@ -1025,6 +1026,43 @@ __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const floa
   }
 }
 
+}  // namespace
+
+// The split-key partial states of attn_fwd_splitkv_noalloc: device memory of
+// the library itself, so that entry point allocates nothing.  Every GPU the
+// library runs on holds its own copy until the process ends, and every call on
+// that GPU reuses it (the contents of the previous call stay; the split
+// kernels write every state the merge reads, so nothing needs clearing).
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (the array's name is a host-side stand-in, not a device
+// address, so only this pointer ever reaches a kernel).
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[64];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_E_DEVICE;
+  if (dev < 64) {
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) {
+      *out = p;
+      return ATTN_OK;
+    }
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  void* p = dev < 64 ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_E_HIP;
+    if (dev < 64) g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -1291,9 +1329,15 @@ extern "C" int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, 
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
-                                int S_kv, int D_h, int causal, float scale, int dtype, void* stream, int kv_len,
-                                int n_split, void* workspace, size_t workspace_bytes) {
+namespace {
+
+// attn_fwd_splitkv's checks and launches for a workspace the caller brings
+// (own_ws = false: null, misaligned, short or overlapping workspaces are
+// rejected) or the library's scratch array (own_ws = true: the array's
+// device address, looked up after the argument checks).
+int splitkv_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q, int S_kv, int D_h,
+                 int causal, float scale, int dtype, void* stream, int kv_len, int n_split, void* workspace,
+                 size_t workspace_bytes, bool own_ws) {
   const int st = validate(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, S_q, kv_len);
   if (st != ATTN_OK) return st;
   size_t need = 0;
@@ -1303,7 +1347,9 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
   const int64_t grid = (int64_t)sc.groups * sc.heads * sc.tl;
   const int64_t rows = (int64_t)B * H * S_q;
   if (grid * n_split > INT32_MAX || (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS > INT32_MAX) return ATTN_E_SPLIT;
-  if (n_split > 1) {
+  if (own_ws) {
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_E_WORKSPACE;
+  } else if (n_split > 1) {
     if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return ATTN_E_WORKSPACE;
     const uint64_t esz = dtype == ATTN_F32 ? 4 : 2;
     const uint64_t nq = (uint64_t)rows * HEAD_DIM * esz, nkv = (uint64_t)B * H * S_kv * HEAD_DIM * esz;
@@ -1314,6 +1360,10 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
   int n_cu = 0;
   const int dv = check_device(&n_cu);
   if (dv != ATTN_OK) return dv;
+  if (own_ws && n_split > 1) {
+    const int sp = scratch_address(&workspace);
+    if (sp != ATTN_OK) return sp;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case ATTN_F32:
@@ -1326,6 +1376,22 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
       return launch_typed<__bf16>(q, k, v, o, B, H, S_q, S_kv, causal, scale, s, S_q, kv_len, n_cu, nullptr,
                                   n_split, workspace);
   }
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, int B, int H, int S_q,
+                                int S_kv, int D_h, int causal, float scale, int dtype, void* stream, int kv_len,
+                                int n_split, void* workspace, size_t workspace_bytes) {
+  return splitkv_impl(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, stream, kv_len, n_split, workspace,
+                      workspace_bytes, false);
+}
+
+extern "C" int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H,
+                                        int S_q, int S_kv, int D_h, int causal, float scale, int dtype,
+                                        void* stream, int kv_len, int n_split) {
+  return splitkv_impl(q, k, v, o, B, H, S_q, S_kv, D_h, causal, scale, dtype, stream, kv_len, n_split, nullptr, 0,
+                      true);
 }
 
 extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int* grid) {
