@@ -33,10 +33,12 @@
  * Arithmetic: Q K^T and P V run on MFMA (bf16/fp16 operands with fp32
  * accumulation for ATTN_BF16/ATTN_F16; true fp32 MFMA for ATTN_F32).  The
  * probabilities P are computed in fp32; on the 16-bit paths they are rounded
- * once to the input type, only as the operand of the P V product, and the row
- * sum l adds the fp32 values before that rounding (so the normalised weights
- * sum to one within the rounding of P: a relative 2^-9 for bf16, 2^-12 for
- * fp16).  No [S_q, S_kv] buffer is written anywhere.
+ * once to the input type, as the operand of the P V product, and the row sum
+ * l adds those rounded values (fp32 accumulation on the matrix cores), so the
+ * output is the exact weighted mean with the weights P V applies; each weight
+ * differs from the fp32 probability by its rounding (a relative 2^-9 for
+ * bf16, 2^-12 for fp16).  ATTN_F32 keeps P and l in fp32.  No [S_q, S_kv]
+ * buffer is written anywhere.
  *
  * Ownership and concurrency: the caller allocates and frees every buffer.  The
  * library allocates no device or host memory, keeps no pointer after it

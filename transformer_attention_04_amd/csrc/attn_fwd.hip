@@ -33,16 +33,20 @@
 // probabilities exp2(s - m) stay in range; in exact arithmetic it cancels
 // between numerator and denominator.  It is set from the row maximum until
 // every row of the wave has one, and afterwards left alone: a block's
-// probabilities are taken with the current offset and only if some lane's sum
-// over the block exceeds 2^15 are the block's scores recomputed, their maximum taken
-// and the offset raised to it when that maximum exceeds it by more than 2^8
-// (then acc and l are rescaled by exp2(m_old - m_new)).  Steady-state blocks
+// probabilities are taken with the current offset and only if some row's sum
+// over the block exceeds 2^16 (or is not finite: an fp16 probability that
+// overflowed) are the block's scores recomputed, their maximum taken and the
+// offset raised to it when that maximum exceeds it by more than 2^8 (then
+// acc and l are rescaled by exp2(m_old - m_new)).  Steady-state blocks
 // therefore need neither the row maximum nor a rescale, and every probability
-// fed to the P V product is <= 2^15, inside the fp16 range.  Probabilities are
-// rounded to bf16/fp16 only as the MFMA operand of the P V product; l sums
-// them in fp32 before that rounding.  fp32 inputs keep fp32 probabilities and
-// take the maximum on every block (their fp32 MFMAs dominate; the lazy 2^8
-// rule still skips most rescales).
+// fed to the P V product is <= 2^16 and finite in fp16.  Probabilities are
+// rounded to bf16/fp16 once, as the MFMA operand of the P V product, and l
+// sums those rounded values on the matrix cores: a 16x16x32 MFMA whose A
+// operand is a fixed pattern of ones and whose B operand is the P operand
+// itself (so the normalised weights are exactly the ones P V applies).  fp32
+// inputs keep fp32 probabilities, sum them with fp32 adds and take the
+// maximum on every block (their fp32 MFMAs dominate; the lazy 2^8 rule still
+// skips most rescales).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -65,7 +69,7 @@ constexpr int MAX_SPLIT = 1024;          // key ranges per call, at most
 constexpr int SPLIT_MIN_KV_TILES = 16;   // the automatic split leaves shorter key chains whole
 constexpr int NTHREADS = 256;  // 4 wavefronts of 64
 constexpr float LAZY_TH = 8.0f;       // log2 headroom before the offset is raised
-constexpr float P_LIMIT = 32768.0f;  // largest per-lane block sum taken without a max
+constexpr float ROW_LIMIT = 65536.0f;  // largest 64-key row sum (16-bit paths) taken without a max
 
 // ---------------------------------------------------------------------------
 // Schedule: blockIdx.x -> (head, query rows [row0, row1)).
@@ -179,9 +183,11 @@ __device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballo
 // raises the exponent offset m only when the tile exceeds it by more than 2^8
 // (then rescales acc and l by exp2(m_old - m_new) for the whole wave), and
 // returns the offset to subtract: 0 while the row has seen no visible key.
+// lx: the 16-bit kernels' matrix-core row-sum accumulator (register 0 is
+// this lane's row), rescaled with l; null for fp32.
 template <int NB>
 __device__ __forceinline__ float online_offset(const f32x16 (&s)[NB], f32x16 (&acc)[2], float& m, float& l,
-                                               const float cc) {
+                                               const float cc, f32x4* lx = nullptr) {
   float mx[NB];
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) {  // one chain per block, in two halves
@@ -206,6 +212,7 @@ __device__ __forceinline__ float online_offset(const f32x16 (&s)[NB], f32x16 (&a
     const float m_new = raise ? xc : m;
     const float alpha = raise ? fast_exp2(m - xc) : 1.f;
     l *= alpha;
+    if (lx) (*lx)[0] *= alpha;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc[0][r] *= alpha;
@@ -229,16 +236,10 @@ __device__ __forceinline__ int v16_off(int row, int c16) {
 // Probabilities of one tile for the 16-bit path: P = exp2(s*c - moff) in fp32,
 // RNE-packed to 16 bits in the B-operand layout of the P V product (pw[kb][u]
 // word q holds keys 8u + 2q, 8u + 2q + 1 of block kb, k-slots 8hf + 2q, +1).
-// Returns this lane's sum of the fp32 values, taken with plain fp32 adds: the
-// packed-pair dot instructions would halve the count, but on gfx950 they wait
-// for the matrix pipe, so while the other wave of the SIMD streams MFMAs they
-// stall this wave's whole in-order instruction stream (fma, exp, cvt and add
-// all run beside the MFMAs).
 template <typename T, int NB>
-__device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, const float moff,
-                                         u32x4 (&pw)[NB][2]) {
+__device__ __forceinline__ void probs16(const f32x16 (&s)[NB], const float cc, const float moff,
+                                        u32x4 (&pw)[NB][2]) {
   typedef Half16<T> H;
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -249,24 +250,58 @@ __device__ __forceinline__ float probs16(const f32x16 (&s)[NB], const float cc, 
         const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], cc, -moff));
         const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cc, -moff));
         pw[kb][u][q] = H::pack2(e0, e1);
-        ls[2 * (q & 1)] += e0;
-        ls[2 * (q & 1) + 1] += e1;
       }
-  return (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
-// One wave's work on one 64-key tile: S^T = K Q^T on MFMA, online-softmax
-// update, O^T += V^T P^T on MFMA.  TWO: the tile's second 32-key block is
-// visible to some row of this wave (false only on causal diagonal tiles and
-// at the cache end).  MASK: some key of the tile is invisible to some row.
-// SPEC: take the probabilities at the current offset first (false for a
-// wave's first tile, whose offsets are not set yet: straight to the maximum).
-// MSET: every lane's offset is known to be set (after a first tile that every
-// row of the wave sees in full), so only the block sums are checked.
+// Row sums of the packed probabilities on the matrix cores.  Step (kb, u) of
+// pw is 64 lanes x 8 values, lane (c, hf) holding 8 of query c's; as the B
+// operand of a 16x16x32 MFMA (B[k][j] at lane j + 16(k/8), element k%8) it is
+// column j = lane % 16 with k-groups from lanes j, j+16, j+32, j+48, i.e.
+// queries j, j+16, j, j+16.  `ones` (A[i][k] at lane i + 16(k/8)) is 1 in
+// rows 0 and 8 for k-groups 0 and 2 and in rows 4 and 12 for k-groups 1 and
+// 3, 0 elsewhere, so C[0][j] and C[8][j] are query j's sum and C[4][j],
+// C[12][j] query j+16's; with C[i][j] at lane j + 16(i/4), register i%4,
+// register 0 of every lane holds its own query's sum over the step's 16 keys
+// (both half-waves' keys).  Returns rs plus the tile's row sums (register 0).
+template <typename T, int NB>
+__device__ __forceinline__ f32x4 rowsum16_acc(const u32x4 (&pw)[NB][2], const typename Half16<T>::vec8& ones,
+                                              f32x4 rs) {
+  typedef Half16<T> H;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) rs = H::mfma16(ones, __builtin_bit_cast(typename H::vec8, pw[kb][u]), rs);
+  return rs;
+}
+
+
+// The A operand of rowsum16 for this lane: ones where (lane % 16) % 8 is 4 *
+// ((lane / 16) % 2) and lane % 4 is 0 (lanes 0, 8, 20, 28, 32, 40, 52, 60).
+template <typename T>
+__device__ __forceinline__ typename Half16<T>::vec8 rowsum_ones(const int lane) {
+  const unsigned w = ((lane & 7) == 4 * ((lane >> 4) & 1) && (lane & 3) == 0) ? Half16<T>::ONE2 : 0u;
+  const u32x4 x = {w, w, w, w};
+  return __builtin_bit_cast(typename Half16<T>::vec8, x);
+}
+
+// The softmax half of one wave's work on one 64-key tile: S^T = K Q^T on
+// MFMA, the online-softmax update and the packed probabilities pw (the B
+// operands of the tile's P V product, pv16).  TWO: the tile's second 32-key
+// block is visible to some row of this wave (false only on causal diagonal
+// tiles and at the cache end).  MASK: some key of the tile is invisible to
+// some row.  SPEC: take the probabilities at the current offset first (false
+// for a wave's first tile, whose offsets are not set yet: straight to the
+// maximum).  MSET: every lane's offset is known to be set (after a first tile
+// that every row of the wave sees in full), so only the block sums are
+// checked.
+// lx: the row sum (register 0), accumulated on the matrix cores; a tile reads
+// its own sum as the increase of lx.  online_offset rescales lx with acc; l is
+// unused (fp32 keeps its sums there).
 template <typename T, bool TWO, bool MASK, bool CAUSAL, bool SPEC = true, bool MSET = false>
-__device__ __forceinline__ void tile16(const char* ks, const char* vs, const typename Half16<T>::vec8 (&qop)[4],
-                                       f32x16 (&acc)[2], float& m, float& l, const float cc, const int kv0,
-                                       const int kv_len, const int pos, const int lane) {
+__device__ __forceinline__ void softmax16(const char* ks, const typename Half16<T>::vec8 (&qop)[4],
+                                          const typename Half16<T>::vec8& ones, f32x16 (&acc)[2], float& m,
+                                          float& l, f32x4& lx, const float cc, const int kv0, const int kv_len,
+                                          const int pos, const int lane, u32x4 (&pw)[TWO ? 2 : 1][2]) {
   typedef Half16<T> H;
   typedef typename H::vec8 vec8;
   constexpr int NB = TWO ? 2 : 1;
@@ -302,17 +337,26 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
   scores(s, kv0);
 
   // Take the probabilities at the current offset.  If some lane's offset is
-  // not set yet (m = -inf: its row has seen no key) or its block sum is out
-  // of range, redo the tile through the maximum: re-read K (s is consumed by
-  // then, so no score register lives across the branch), raise the offset,
-  // recompute.  The test is per lane and comes after the probabilities, so
-  // the steady case is one straight-line block; one call site keeps a single
-  // rescale point for acc.
-  u32x4 pw[NB][2];
-  float ts;
+  // not set yet (m = -inf: its row has seen no key) or its row's block sum is
+  // out of range (above 2^16, or not finite), redo the tile through the
+  // maximum: re-read K (s is consumed by then, so no score register lives
+  // across the branch), raise the offset, recompute.  The test is per lane
+  // and comes after the probabilities, so the steady case is one
+  // straight-line block; one call site keeps a single rescale point for acc.
   if constexpr (SPEC) {
-    ts = probs16<T, NB>(s, cc, m, pw);
-    if (any_lane(ts > P_LIMIT || (!MSET && m == -INFINITY))) {
+    probs16<T, NB>(s, cc, m, pw);
+    f32x4 lnew = rowsum16_acc<T, NB>(pw, ones, lx);
+    const float ts = lnew[0] - lx[0];  // this tile's row sum (>= 0, or inf / NaN)
+    // Out of range: above 2^16, infinite, or NaN.  A NaN appears when an fp16
+    // probability overflowed (inf) and meets a zero of the ones pattern in
+    // another row's sum, so every lane of that pair may hold NaN; the sums are
+    // never negative, so comparing the bit patterns as unsigned integers
+    // catches +inf and NaN of either sign whatever the compiler assumes about
+    // NaN (the device code is built with -fno-honor-nans).  lx grows by at
+    // most 2^16 per tile, so the increase is exact to far better than the
+    // limit.
+    const bool out_of_range = __float_as_uint(ts) > __float_as_uint(ROW_LIMIT);
+    if (any_lane(out_of_range || (!MSET && m == -INFINITY))) {
       asm volatile("" ::: "memory");
       // An opaque copy of kv0: the masks are recomputed here rather than the
       // first pass's 32 lane masks being kept in scalar registers meanwhile.
@@ -320,50 +364,63 @@ __device__ __forceinline__ void tile16(const char* ks, const char* vs, const typ
       asm volatile("" : "+v"(k0));
       f32x16 s2[NB];
       scores(s2, k0);
-      const float moff = online_offset<NB>(s2, acc, m, l, cc);  // may rescale acc and l
-      ts = probs16<T, NB>(s2, cc, moff, pw);
+      const float moff = online_offset<NB>(s2, acc, m, l, cc, &lx);  // may rescale acc and lx
+      probs16<T, NB>(s2, cc, moff, pw);
+      lnew = rowsum16_acc<T, NB>(pw, ones, lx);
     }
+    lx = lnew;
   } else {
-    const float moff = online_offset<NB>(s, acc, m, l, cc);  // may rescale acc and l
-    ts = probs16<T, NB>(s, cc, moff, pw);
+    const float moff = online_offset<NB>(s, acc, m, l, cc, &lx);  // may rescale acc and lx
+    probs16<T, NB>(s, cc, moff, pw);
+    lx = rowsum16_acc<T, NB>(pw, ones, lx);
   }
-  l += ts;
+}
 
-  // V^T operands, read transposed from the [key][d] tile after the softmax:
-  // not live during it, the 16-bit kernel fits three workgroups per CU (168
-  // VGPRs), whose third wave per SIMD hides the reads' latency.  Operand
-  // (kb, u, dt), k-slot 8hf + e, holds
-  // V[32kb + 16u + 8(e/4) + 4hf + e%4][32dt + c]: source lane s of each
-  // 16-lane group reads row kbase + s/4, columns d0 + 4(s%4) .. +3.
-  vec8 va[NB][2][2];
-  {
-    const int g = lane >> 4, sl = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
-          const int c16 = d0 >> 3, half = (d0 >> 2) & 1;
-          const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row + 8, c16) + 8 * half));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          va[kb][u][dt] = __builtin_bit_cast(vec8, aw);
-        }
-  }
-
-  // O^T += V^T P^T: step (kb, u) contracts keys 32kb + 16u .. +15.
+// The P V half: O^T += V^T P^T for the tile whose probabilities are pw.  V^T
+// operands are read transposed from the [key][d] tile: operand (kb, u, dt),
+// k-slot 8hf + e, holds V[32kb + 16u + 8(e/4) + 4hf + e%4][32dt + c]: source
+// lane s of each 16-lane group reads row kbase + s/4, columns d0 + 4(s%4)
+// .. +3.  Step (kb, u) contracts keys 32kb + 16u .. +15.
+template <typename T, bool TWO>
+__device__ __forceinline__ void pv16(const char* vs, const u32x4 (&pw)[TWO ? 2 : 1][2], f32x16 (&acc)[2],
+                                     const int lane) {
+  typedef Half16<T> H;
+  typedef typename H::vec8 vec8;
+  constexpr int NB = TWO ? 2 : 1;
+  const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      vec8 va[2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+        const int c16 = d0 >> 3, half = (d0 >> 2) & 1;
+        const int row = 32 * kb + 16 * u + 4 * (g >> 1) + (sl >> 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row, c16) + 8 * half));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vs + v16_off(row + 8, c16) + 8 * half));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        va[dt] = __builtin_bit_cast(vec8, aw);
+      }
       const vec8 b = __builtin_bit_cast(vec8, pw[kb][u]);
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) acc[dt] = H::mfma(va[kb][u][dt], b, acc[dt]);
+      for (int dt = 0; dt < 2; ++dt) acc[dt] = H::mfma(va[dt], b, acc[dt]);
     }
+}
+
+// One wave's whole work on one 64-key tile: softmax16, then pv16 (the V^T
+// operands are read after the softmax: not live during it, the 16-bit kernel
+// fits three workgroups per CU at 168 VGPRs).
+template <typename T, bool TWO, bool MASK, bool CAUSAL, bool SPEC = true, bool MSET = false>
+__device__ __forceinline__ void tile16(const char* ks, const char* vs, const typename Half16<T>::vec8 (&qop)[4],
+                                       const typename Half16<T>::vec8& ones, f32x16 (&acc)[2], float& m, float& l,
+                                       f32x4& lx, const float cc, const int kv0, const int kv_len, const int pos,
+                                       const int lane) {
+  u32x4 pw[TWO ? 2 : 1][2];
+  softmax16<T, TWO, MASK, CAUSAL, SPEC, MSET>(ks, qop, ones, acc, m, l, lx, cc, kv0, kv_len, pos, lane, pw);
+  pv16<T, TWO>(vs, pw, acc, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,6 +536,9 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 //
 // Pipeline: a stage holds KS consecutive 64-key tiles of K, then of V.  With
 // three stages two stages are in flight while one is computed; with two, one.
+// The 16-bit one-group kernel's full-tile loop runs each tile's P V one step
+// late, beside the next tile's probabilities: there the previous tile stays
+// resident and one stage is in flight.
 //
 // VARLEN: each sequence has its own key length, read from p.kv_lens (key
 // padding); a row that then sees no key gets zeros.
@@ -568,7 +628,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // lane's 16-byte chunk in a K row and a V row (swizzled).  The clamped
   // copies recompute these from an opaque copy of the thread index, so none
   // of them stays live across the key loop.
-  auto copy_geom = [&](const int i, const int t, int& row, uint32_t& kc, uint32_t& vc) {
+  auto copy_geom = [&](const int i, const int t, int& row, uint32_t& kc, uint32_t& vc) __attribute__((always_inline)) {
     const int ln = t & 63, wv = t >> 6;
     row = 64 * (wv >> 2) + RPC * (4 * i + (wv & 3)) + ln / LPR;
     const int ph = ln % LPR;
@@ -604,7 +664,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // stage: consecutive copies go in pairs (dma16_pair).
   constexpr int CSTEP = RPC * 4 * ROWB;
   static_assert(CSTEP == 4096 && NCP % 2 == 0, "paired tile copies");
-  auto issue_full = [&](char* st, int super) {
+  auto issue_full = [&](char* st, int super) __attribute__((always_inline)) {
     const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     const int64_t off = (int64_t)super * KS * BN * ROWB;
 #pragma unroll
@@ -613,7 +673,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
       dma16_pair(vl[i] + (off + 2048), mv + i * CSTEP + 2048);
     }
   };
-  auto issue = [&](char* st, int super) {
+  auto issue = [&](char* st, int super) __attribute__((always_inline)) {
     const int kv0 = super * KS * BN;
     if (kv0 + KS * BN <= kv_len) {
       issue_full(st, super);
@@ -654,7 +714,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
       dma16(qb + ((int64_t)min(wrow0 + row, row1 - 1) * ROWB + cb), mq + i * 1024);
     }
   }
-  auto read_q = [&]() {
+  auto read_q = [&]() __attribute__((always_inline)) {
     const char* qs = qst + wslab;
     if constexpr (F32) {
 #pragma unroll
@@ -681,10 +741,13 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
     acc[1][r] = 0.f;
   }
   float m = -INFINITY;  // exponent offset (log2 units), per row
-  float l = 0.f;        // this lane's share of the row sum
+  float l = 0.f;        // row sum: 16-bit, the whole row's; fp32, this lane's share
+  f32x4 lx = {0.f, 0.f, 0.f, 0.f};  // 16-bit: row sums of optimistic tiles (register 0)
+  // A operand of the 16-bit row sums (rowsum16).
+  const auto ones = rowsum_ones<typename std::conditional<F32, __bf16, T>::type>(lane);
   const float cc = p.c;
 
-  auto compute = [&](const char* st, int super) {
+  auto compute = [&](const char* st, int super) __attribute__((always_inline)) {
     const int t = super * KS + kh;
     if (t >= n_tiles) return;
     const int kv0 = t * BN;
@@ -712,14 +775,14 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
     } else {
       if (blk1) {
         if (need_mask)
-          tile16<T, true, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, true, true, CAUSAL>(ks, vs, qop, ones, acc, m, l, lx, cc, kv0, kv_len, pos, lane);
         else
-          tile16<T, true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, true, false, CAUSAL>(ks, vs, qop, ones, acc, m, l, lx, cc, kv0, kv_len, pos, lane);
       } else {
         if (need_mask)
-          tile16<T, false, true, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, false, true, CAUSAL>(ks, vs, qop, ones, acc, m, l, lx, cc, kv0, kv_len, pos, lane);
         else
-          tile16<T, false, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
+          tile16<T, false, false, CAUSAL>(ks, vs, qop, ones, acc, m, l, lx, cc, kv0, kv_len, pos, lane);
       }
     }
   };
@@ -736,25 +799,34 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   if (CAUSAL) t_full = min(t_full, (row0 + shift + 1) / BN);
   int j_full = min(t_full / KS, min(kv_len / (KS * BN), n_super) - (NS - 1));
   j_full = j_full > 0 ? j_full - j_full % NS : 0;
-  auto compute_full = [&](const char* st, int super, auto spec) {
+  auto compute_full = [&](const char* st, int super, auto spec) __attribute__((always_inline)) {
     const char* ks = st + kh * TILE;
     const char* vs = st + KS * TILE + kh * TILE;
     const int kv0 = (super * KS + kh) * BN;
     if constexpr (F32)
       tile32<true, false, CAUSAL>(ks, vs, qop, acc, m, l, cc, kv0, kv_len, pos, lane);
     else
-      tile16<T, true, false, CAUSAL, decltype(spec)::value, decltype(spec)::value>(ks, vs, qop, acc, m, l, cc, kv0,
-                                                                                  kv_len, pos, lane);
+      tile16<T, true, false, CAUSAL, decltype(spec)::value, decltype(spec)::value>(ks, vs, qop, ones, acc, m, l, lx,
+                                                                                  cc, kv0, kv_len, pos, lane);
   };
-  const std::true_type spec;       // offsets set (every lane): speculate
-  const std::false_type first;     // a wave's first tile
+  const std::true_type spec;    // offsets set (every lane): speculate
+  const std::false_type first;  // a wave's first tile
+
+  if (n_super > 0) issue(st0, 0);
+  if (NS == 3 && n_super > 1) issue(st1, 1);
+  // The Q rows and super-tile 0 (copied before super-tile 1).
+  if (NS == 3 && n_super > 1)
+    wait_vmem<2 * NCP>();
+  else
+    wait_vmem<0>();
+  read_q();
 
   int j = 0;
   if constexpr (NS == 3) {
     // Stage j % 3 holds super-tile j.  At step j super-tiles j and j+1 may be
     // in flight: wait for j, barrier (everyone is done with j-1), start j+2
     // into j-1's stage, compute j.
-    auto sync = [&](char* nxt, int j) {
+    auto sync = [&](char* nxt, int j) __attribute__((always_inline)) {
       if (j + 1 < n_super)
         wait_vmem<2 * NCP>();
       else
@@ -762,35 +834,80 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
       barrier_keep_dma();
       if (j + 2 < n_super) issue(nxt, j + 2);
     };
-    if (n_super > 0) issue(st0, 0);
-    if (n_super > 1) issue(st1, 1);
-    // The Q rows and super-tile 0 (copied before super-tile 1).
-    if (n_super > 1)
-      wait_vmem<2 * NCP>();
-    else
-      wait_vmem<0>();
-    read_q();
-    auto sync_full = [&](char* nxt, int j) {
-      wait_vmem<2 * NCP>();
-      barrier_keep_dma();
-      issue_full(nxt, j + 2);
-    };
-    if (j_full > 0) {  // the first group: its first tile sets the offsets
-      sync_full(st2, 0);
-      compute_full(st0, 0, first);
-      sync_full(st0, 1);
-      compute_full(st1, 1, spec);
-      sync_full(st1, 2);
-      compute_full(st2, 2, spec);
-      j = 3;
-    }
-    for (; j < j_full; j += 3) {
-      sync_full(st2, j);
-      compute_full(st0, j, spec);
-      sync_full(st0, j + 1);
-      compute_full(st1, j + 1, spec);
-      sync_full(st1, j + 2);
-      compute_full(st2, j + 2, spec);
+    if constexpr (!F32) {
+      // 16-bit full tiles with the P V product one step behind: step j takes
+      // tile j - 1's P V and then tile j's softmax, so the matrix cores have
+      // independent work (the P V MFMAs) while the probabilities of tile j
+      // are computed.  Tile j - 1 must stay in its stage during step j, so
+      // copies run one tile ahead: step j starts tile j + 1 into the stage of
+      // tile j - 2 (free once every wave has passed this step's barrier).
+      u32x4 pw_prev[2][2];
+      auto step = [&](char* cur, char* prev, char* nxt, int j) __attribute__((always_inline)) {
+        wait_vmem<0>();
+        barrier_keep_dma();
+        issue_full(nxt, j + 1);
+        // The P V MFMAs come first in the source so that they share the
+        // basic block of this tile's probabilities (the fallback test ends
+        // it); the scheduler spreads them over the probability arithmetic.
+        pv16<T, true>(prev + TILE, pw_prev, acc, lane);
+        u32x4 pw[2][2];
+        softmax16<T, true, false, CAUSAL, true, true>(cur, qop, ones, acc, m, l, lx, cc, j * BN, kv_len, pos, lane,
+                                                       pw);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) pw_prev[kb][u] = pw[kb][u];
+      };
+      if (j_full > 0) {
+        // Step 0: tiles 0 and 1 are in flight; the first tile sets the offsets.
+        wait_vmem<2 * NCP>();
+        barrier_keep_dma();
+        softmax16<T, true, false, CAUSAL, false, false>(st0, qop, ones, acc, m, l, lx, cc, 0, kv_len, pos, lane,
+                                                         pw_prev);
+        for (j = 1; j < j_full; j += 3) {
+          step(st1, st0, st2, j);
+          if (j + 1 >= j_full) {
+            j += 1;
+            break;
+          }
+          step(st2, st1, st0, j + 1);
+          if (j + 2 >= j_full) {
+            j += 2;
+            break;
+          }
+          step(st0, st2, st1, j + 2);
+        }
+        // j == j_full, a multiple of 3: tile j is in flight, tile j - 1's P V
+        // is pending.  Barrier (every wave is done with tile j - 2), start
+        // tile j + 1 into its stage, then tile j - 1's P V; the general steps
+        // below continue with two tiles in flight.
+        barrier_keep_dma();
+        if (j + 1 < n_super) issue(st1, j + 1);
+        pv16<T, true>(st2 + TILE, pw_prev, acc, lane);
+      }
+    } else {
+      auto sync_full = [&](char* nxt, int j) __attribute__((always_inline)) {
+        wait_vmem<2 * NCP>();
+        barrier_keep_dma();
+        issue_full(nxt, j + 2);
+      };
+      if (j_full > 0) {  // the first group: its first tile sets the offsets
+        sync_full(st2, 0);
+        compute_full(st0, 0, first);
+        sync_full(st0, 1);
+        compute_full(st1, 1, spec);
+        sync_full(st1, 2);
+        compute_full(st2, 2, spec);
+        j = 3;
+      }
+      for (; j < j_full; j += 3) {
+        sync_full(st2, j);
+        compute_full(st0, j, spec);
+        sync_full(st0, j + 1);
+        compute_full(st1, j + 1, spec);
+        sync_full(st1, j + 2);
+        compute_full(st2, j + 2, spec);
+      }
     }
     for (; j < n_super; j += 3) {
       sync(st2, j);
@@ -804,15 +921,12 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
     }
   } else {
     // Two stages: wait for j, barrier, start j+1 into j-1's stage, compute j.
-    auto sync = [&](char* nxt, int j) {
+    auto sync = [&](char* nxt, int j) __attribute__((always_inline)) {
       wait_vmem<0>();
       barrier_keep_dma();
       if (j + 1 < n_super) issue(nxt, j + 1);
     };
-    if (n_super > 0) issue(st0, 0);
-    wait_vmem<0>();  // the Q rows (and super-tile 0)
-    read_q();
-    auto sync_full = [&](char* nxt, int j) {
+    auto sync_full = [&](char* nxt, int j) __attribute__((always_inline)) {
       wait_vmem<0>();
       barrier_keep_dma();
       issue_full(nxt, j + 1);
@@ -838,6 +952,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
       compute(st1, j + 1);
     }
   }
+  if constexpr (!F32) l = lx[0];
 
   if constexpr (KS == 2) {
     // Merge the odd-tile waves' state into the even-tile waves (same query
@@ -888,7 +1003,9 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // of the second-to-last key tile (every wave has passed it and no copy
   // targets it any more); with the key split, the wave's own part of the
   // merge area, which it has read.
-  const float lt = l + other_half(l);
+  // The row's sum: 16-bit lanes hold the whole row's already (the matrix-core
+  // row sums add both half-waves' keys); fp32 lanes hold their half's.
+  const float lt = F32 ? l + other_half(l) : l;
   if constexpr (SPLIT) {
     // This key range's state of each valid row, one row per lane: fp32 acc
     // (its half of the columns per half-wave), and (m, l) from half-wave 0.

@@ -13,6 +13,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -77,8 +78,12 @@ struct Half16;
 template <>
 struct Half16<__bf16> {
   typedef bf16x8 vec8;
+  static constexpr unsigned ONE2 = 0x3f803f80u;  // two 1.0 values
   __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ unsigned pack2(float x, float y) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
@@ -88,8 +93,12 @@ struct Half16<__bf16> {
 template <>
 struct Half16<_Float16> {
   typedef f16x8 vec8;
+  static constexpr unsigned ONE2 = 0x3c003c00u;  // two 1.0 values
   __device__ static __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ unsigned pack2(float x, float y) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, f16x2));
