@@ -16,14 +16,20 @@
 //   chunks XOR-swizzled per row, the layout of the attention kernels' K
 //   tiles), two stages in flight-and-compute.  Both operands are contiguous
 //   in K, so the MFMA computes C^T = W x^T: lane l of a 32 x 32 block owns
-//   one row of C (row l % 32) and 16 of its columns, and the epilogue writes
-//   whole 8-byte pieces of output rows.  Wave (wm, wn) = (wave % 4, wave / 4)
+//   one row of C (row l % 32) and 16 of its columns; the accumulators start
+//   from the bias, and the epilogue goes through LDS so that every store is a
+//   whole 16-byte piece of an output row.  Wave (wm, wn) = (wave % 4, wave / 4)
 //   owns rows 64 wm .. +63 and columns 128 wn .. +127 of the tile: 2 x 4
 //   blocks of v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation (128
 //   accumulator registers of the 256 each of the two waves per SIMD has).
-//   Tiles are dealt so that the 12 (for d = 1024) column tiles of one row
-//   block run back to back on one XCD, which then reads that block of x from
-//   its own L2.
+//   Tiles are dealt to the XCDs (workgroups go round-robin over the 8 XCDs)
+//   as 8 rectangular parts of the tile grid: cg column groups by 8 / cg row
+//   groups.  Inside a part the tiles run row block major, so the 32
+//   workgroups an XCD holds at once cover about 32 / c row blocks and c
+//   column tiles (c = column tiles per part) and read each of those x and W
+//   blocks once from beyond the XCD's L2 while they walk K together; the
+//   host picks the cg that makes 32 / c + c, the blocks fetched per such
+//   round, smallest.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -56,6 +62,9 @@ struct ProjParams {
   int S, H;
   int tiles_n;    // column tiles
   int tiles;      // total tiles
+  int cg;         // column groups of the XCD parts (1, 2, 4 or 8), or 0: plain row-major order
+  int prows;      // row blocks per part
+  int pcols;      // column tiles per part
 };
 
 template <typename T>
@@ -64,12 +73,18 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
   typedef typename H16::vec8 vec8;
   __shared__ __attribute__((aligned(16))) char lds[PLDS];
 
-  // Tile of this workgroup: with a multiple of 8 tiles, XCD x (blocks dealt
-  // round-robin) takes a contiguous run of tile indices, row block major.
-  int L = blockIdx.x;
-  if ((p.tiles & 7) == 0) L = (blockIdx.x & 7) * (p.tiles >> 3) + (blockIdx.x >> 3);
-  const int mt = L / p.tiles_n;
-  const int nt = L - mt * p.tiles_n;
+  // Tile of this workgroup: block b runs on XCD x = b % 8 as that XCD's
+  // i = b / 8-th tile; part x is column group x % cg, row group x / cg.
+  int mt, nt;
+  if (p.cg) {
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int ri = i / p.pcols;
+    mt = (x / p.cg) * p.prows + ri;
+    nt = (x % p.cg) * p.pcols + (i - ri * p.pcols);
+  } else {
+    mt = blockIdx.x / p.tiles_n;
+    nt = blockIdx.x - mt * p.tiles_n;
+  }
   const int m0 = mt * PM, n0 = nt * PN;
 
   const int tid = threadIdx.x;
@@ -82,37 +97,56 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
   // l % 8 and fetches the logical chunk the row's swizzle maps there: with
   // swizzle (r & 7) ^ ((r >> 3) & 1) = (l / 8) ^ (i & 1) that is chunk
   // (l % 8) ^ (l / 8) ^ (i & 1).  Rows past the matrix end re-read its last
-  // row (finite data, never stored).  Source addresses are recomputed per
-  // copy rather than held in registers.
-  const int crow = 32 * wave + lane / 8;
-  const int cch = (lane % 8) ^ (lane / 8);
-  const char* const xb = reinterpret_cast<const char*>(p.x);
-  const char* const wb = reinterpret_cast<const char*>(p.w);
-  const int64_t rowb = (int64_t)p.K * 2;
-  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(32 * wave * PROWB));
-  auto issue = [&](int stage, int kt) {
-    const uint32_t mx = lds_addr(lds) + stage * PHALF + wdst, mw = mx + 2 * PHALF;
-    const int64_t off = (int64_t)kt * PROWB;
-    // An opaque copy of the row: otherwise the eight row addresses are hoisted
-    // out of the K loop and held (16 registers) for its whole length.
-    int row = crow;
-    asm volatile("" : "+v"(row));
+  // row (finite data, never stored).  The eight source addresses of stage 0
+  // are kept (16 registers); stage kt adds kt * 128 bytes.
+  const char* src[8];
+  {
+    const int crow = 32 * wave + lane / 8;
+    const int cch = (lane % 8) ^ (lane / 8);
+    const char* const xb = reinterpret_cast<const char*>(p.x);
+    const char* const wb = reinterpret_cast<const char*>(p.w);
+    const int64_t rowb = (int64_t)p.K * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = row + 8 * i;
-      const int64_t col = off + 16 * (cch ^ (i & 1));
-      dma16(xb + min(m0 + r, p.M - 1) * rowb + col, mx + i * 8 * PROWB);
-      dma16(wb + min(n0 + r, p.N - 1) * rowb + col, mw + i * 8 * PROWB);
+      const int r = crow + 8 * i;
+      const int col = 16 * (cch ^ (i & 1));
+      src[2 * i] = xb + min(m0 + r, p.M - 1) * rowb + col;
+      src[2 * i + 1] = wb + min(n0 + r, p.N - 1) * rowb + col;
+    }
+  }
+  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(32 * wave * PROWB));
+  auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
+    const uint32_t mx = lds_addr(lds) + stage * PHALF + wdst, mw = mx + 2 * PHALF;
+    const int64_t off = (int64_t)kt * PROWB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16(src[2 * i] + off, mx + i * 8 * PROWB);
+      dma16(src[2 * i + 1] + off, mw + i * 8 * PROWB);
     }
   };
 
+  // Accumulators start from the bias: block (nb, mb) register r holds
+  // C[m][n] with m = m0 + 64wm + 32mb + c and n = n0 + 128wn + 32nb +
+  // 8(r/4) + 4hf + r%4, so registers 4q .. 4q+3 take 4 consecutive bias
+  // values (one 8-byte load; N is a multiple of 64, so n < N covers all 4).
   f32x16 acc[4][2];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + 128 * wn + 32 * nb + 8 * q + 4 * hf;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (p.bias && n < p.N) {
+        const u32x2 braw = *reinterpret_cast<const u32x2*>(p.bias + n);
+        const T* bt = reinterpret_cast<const T*>(&braw);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+        for (int e = 0; e < 4; ++e) bv[e] = (float)bt[e];
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nb][mb][4 * q + e] = bv[e];
+    }
 
   // Operand rows 64wm + 32mb + c (x) and 128wn + 32nb + c (W) all have the
   // swizzle sw = (c & 7) ^ ((c >> 3) & 1), so k-step t (chunk 4hf + t, i.e.
@@ -131,7 +165,10 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
     xa[t] = lbase + (64 * wm + c) * PROWB + ch;
     wa[t] = lbase + 2 * PHALF + (128 * wn + c) * PROWB + ch;
   }
-  auto compute = [&](int stage) {
+  // One stage of MFMAs; after the first k-step's MFMAs are issued, `mid`
+  // runs (the next stage's copies: their address arithmetic then overlaps
+  // the matrix work instead of preceding it).
+  auto compute = [&](int stage, auto mid) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       vec8 xo[2], wo[4];
@@ -143,58 +180,60 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = H16::mfma(wo[nb], xo[mb], acc[nb][mb]);
+      if (t == 0) mid();
     }
   };
 
   // Two stages: wait for stage kt (own copies), barrier (every wave's copies
-  // of kt have landed and every wave is done with kt - 1), start kt + 1 into
-  // kt - 1's buffer, compute kt.
+  // of kt have landed and every wave is done with kt - 1), compute kt and,
+  // inside it, start kt + 1 into kt - 1's buffer.
   const int n_k = p.K / PK;
   issue(0, 0);
   for (int kt = 0; kt < n_k; ++kt) {
     wait_vmem<0>();
     barrier_keep_dma();
-    if (kt + 1 < n_k) issue((kt + 1) & 1, kt + 1);
-    compute(kt & 1);
+    compute(kt & 1, [&]() __attribute__((always_inline)) {
+      if (kt + 1 < n_k) issue((kt + 1) & 1, kt + 1);
+    });
   }
 
-  // Epilogue: block (nb, mb) register r holds C[m][n] with m = m0 + 64wm +
-  // 32mb + c and n = n0 + 128wn + 32nb + 8(r/4) + 4hf + r%4.  Blocks 2g and
-  // 2g+1 are the 64 columns n_g = n0 + 128wn + 64g .. +63: one head of one of
-  // q, k, v (d is a multiple of 64); registers 4gq .. 4gq+3 are 4 consecutive
-  // columns, stored as one 8-byte piece of the output row.
+  // Epilogue through LDS (the stage buffers are free once every wave is past
+  // its last stage): wave w rounds its 64 x 128 block of C to T and writes it
+  // to its own 16 KB, rows of 256 bytes; then each lane reads back whole
+  // 16-byte pieces of output rows and stores them, 16 lanes per row of the
+  // block (two heads of 128 bytes each: full cache lines).  Row rr keeps
+  // 16-byte chunk j at chunk j ^ (rr & 15), and rows 16..31 of each 32 swap
+  // the two 8-byte halves of a chunk, so that neither the 8-byte writes (32
+  // rows, one column group) nor the 16-byte reads (one row) meet a bank twice.
+  __syncthreads();
+  char* const ow = lds + wave * (64 * 256);
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int ng = n0 + 128 * wn + 64 * g;
-    if (ng >= p.N) continue;
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 32 * mb + c, ch = 4 * nb + q;
+        const f32x16& a = acc[nb][mb];
+        const u32x2 wv = {H16::pack2(a[4 * q], a[4 * q + 1]), H16::pack2(a[4 * q + 2], a[4 * q + 3])};
+        *reinterpret_cast<u32x2*>(ow + rr * 256 + ((ch ^ (rr & 15)) << 4) + ((hf ^ (rr >> 4 & 1)) << 3)) = wv;
+      }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int rr = 4 * i + lane / 16, ch = lane % 16;
+    u32x4 v = *reinterpret_cast<const u32x4*>(ow + rr * 256 + ((ch ^ (rr & 15)) << 4));
+    if (rr >> 4 & 1) v = (u32x4){v[2], v[3], v[0], v[1]};
+    const int m = m0 + 64 * wm + rr;
+    const int ng = n0 + 128 * wn + 64 * (ch / 8);
+    if (m >= p.M || ng >= p.N) continue;
     const int which = ng / p.K;
     const int h = (ng - which * p.K) >> 6;
-    T* const ob = p.out[which];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = m0 + 64 * wm + 32 * mb + c;
-      if (m >= p.M) continue;
-      const int bb = m / p.S, s = m - bb * p.S;
-      T* const orow = ob + (((int64_t)bb * p.H + h) * p.S + s) * 64;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const f32x16& a = acc[2 * g + j][mb];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int e0 = 32 * j + 8 * gq + 4 * hf;
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (p.bias) {
-            const u32x2 braw = *reinterpret_cast<const u32x2*>(p.bias + ng + e0);
-            const T* bt = reinterpret_cast<const T*>(&braw);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[e] = (float)bt[e];
-          }
-          const u32x2 wv = {H16::pack2(a[4 * gq] + bv[0], a[4 * gq + 1] + bv[1]),
-                            H16::pack2(a[4 * gq + 2] + bv[2], a[4 * gq + 3] + bv[3])};
-          *reinterpret_cast<u32x2*>(orow + e0) = wv;
-        }
-      }
-    }
+    const int bb = m / p.S, sq = m - bb * p.S;
+    // (selected, not indexed: an indexed kernel-argument array is a memory load)
+    T* const ob = which == 0 ? p.out[0] : which == 1 ? p.out[1] : p.out[2];
+    T* const orow = ob + (((int64_t)bb * p.H + h) * p.S + sq) * 64;
+    *reinterpret_cast<u32x4*>(orow + 8 * (ch % 8)) = v;
   }
 }
 
@@ -214,7 +253,24 @@ int launch_proj(const void* x, const void* w, const void* bias, void* q, void* k
   p.S = S;
   p.H = H;
   p.tiles_n = (p.N + PN - 1) / PN;
-  p.tiles = ((p.M + PM - 1) / PM) * p.tiles_n;
+  const int tiles_m = (p.M + PM - 1) / PM;
+  p.tiles = tiles_m * p.tiles_n;
+  // XCD parts: the cg (dividing the column tiles, 8 / cg dividing the row
+  // blocks) with the fewest blocks fetched per round of 32 workgroups.
+  p.cg = 0;
+  p.prows = p.pcols = 0;
+  double best = 0;
+  for (int cg = 1; cg <= 8; cg *= 2) {
+    if (p.tiles_n % cg || tiles_m % (8 / cg)) continue;
+    const int c = p.tiles_n / cg;
+    const double cost = (c >= 32 ? 1.0 : 32.0 / c) + (c >= 32 ? 32.0 : c);
+    if (!p.cg || cost < best) {
+      best = cost;
+      p.cg = cg;
+      p.pcols = c;
+      p.prows = tiles_m / (8 / cg);
+    }
+  }
   hipLaunchKernelGGL((qkv_proj_kernel<T>), dim3(p.tiles), dim3(PTHREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
