@@ -1,8 +1,8 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library.
  *
- * The operation is Eq. A on the page "Shape-Aware Attention" (section
- * "Inspiration"): O = softmax(Q K^T * scale) V, optionally with a causal mask,
+ * The operation is the attention equation on the page "Shape-Aware Attention"
+ * (section "Inspiration"): O = softmax(Q K^T * scale) V, optionally with a causal mask,
  * computed with online softmax -- a running row maximum, running row sum and
  * rescaled fp32 accumulator carried across key/value blocks, so the
  * [B, H, S_q, S_kv] score matrix never exists (page "GPU Kernel for a
@@ -22,7 +22,7 @@
  * (round-to-nearest-even from the fp32 accumulator).  Every base pointer must be
  * 16-byte aligned; o must not overlap q, k or v.  D_h must be 64.
  *
- * scale multiplies q.k before the softmax; pass 1/sqrt(D_h) for Eq. A.  Any
+ * scale multiplies q.k before the softmax; pass 1/sqrt(D_h) for the equation as printed.  Any
  * finite value is accepted (0 gives the plain mean of the visible values).
  *
  * Causal masking is bottom-right aligned: query row i sits at absolute
@@ -85,8 +85,8 @@ enum attn_status {
 
 /*
  * attn_fwd -- O = softmax(Q K^T * scale [+ causal mask]) V over the whole
- * K/V (kv_len = S_kv).  Eq. A, page "Shape-Aware Attention", section
- * "Inspiration"; online softmax as on the page "GPU Kernel for a Transformer
+ * K/V (kv_len = S_kv).  The attention equation of page "Shape-Aware
+ * Attention", section "Inspiration"; online softmax as on the page "GPU Kernel for a Transformer
  * Layer", section "What we learned"; causal masking inside the kernel as in
  * that page's section "How we built it".
  *   q, k, v, o : device pointers, layouts above.

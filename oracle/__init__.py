@@ -5,12 +5,12 @@ leg may import this package.  The product path (``transformer_attention_04_amd``
 never imports it, and this package imports nothing from the product path.
 
 The arithmetic lives in ``attn_oracle.c`` (plain C, IEEE double, libm ``exp``):
-the explicit definition of Eq. A on the page "Shape-Aware Attention" (section
-"Inspiration"), softmax(Q K^T * scale) V, one query row at a time, with the
+the explicit definition of the attention equation on the page "Shape-Aware
+Attention" (section "Inspiration"), softmax(Q K^T * scale) V, one query row at a time, with the
 causal rule "key j visible to query i iff j <= kv_len - S_q + i".  This module
 only marshals numpy arrays into it.
 
-``attention_varlen`` is Eq. A for a batch of sequences of different lengths
+``attention_varlen`` is the attention equation for a batch of sequences of different lengths
 padded to one K/V capacity: per sequence, the same function on its own K/V
 prefix (a slice), with the bottom-right causal rule of that sequence's length
 and zeros for a query row that sees no key.  ``kv_append`` is the K/V cache
@@ -93,7 +93,7 @@ def _f32(x) -> np.ndarray:
 def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
               kv_len: int | None = None, rows=None, threads: int = 0,
               lib=None) -> np.ndarray:
-    """Eq. A in fp64.  q: [B,H,S_q,D], k/v: [B,H,S_kv,D] (float32 values, or torch
+    """The attention equation in fp64.  q: [B,H,S_q,D], k/v: [B,H,S_kv,D] (float32 values, or torch
     CPU tensors of any float dtype, promoted exactly).  scale None -> 1/sqrt(D).
     kv_len None -> S_kv.  rows: optional query-row indices computed for every
     (b,h); the result then has shape [B,H,len(rows),D].  Returns float64."""
@@ -126,7 +126,7 @@ def attention(q, k, v, *, causal: bool = False, scale: float | None = None,
 
 def attention_varlen(q, k, v, kv_lens, *, causal: bool = False, scale: float | None = None,
                      threads: int = 0, lib=None) -> np.ndarray:
-    """Eq. A per sequence of a padded batch (key padding).  q: [B,H,S_q,D],
+    """The attention equation per sequence of a padded batch (key padding).  q: [B,H,S_q,D],
     k/v: [B,H,S_kv,D]; sequence b attends only to its first L_b K/V rows,
     L_b = kv_lens[b] clamped into [0, S_kv].  Causal: query row i of sequence
     b sits at position L_b - S_q + i (bottom-right, as in ``attention``) and

@@ -6,7 +6,7 @@
  * helper with the HIP library; neither includes or links the other.
  *
  * What it computes (page "Shape-Aware Attention", section "Inspiration",
- * Eq. A: Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V), written out as its
+ * the attention equation: Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V), written out as its
  * plain definition with an explicit softmax, one query row at a time:
  *
  *   p_i   = kv_len - S_q + i          absolute position of query row i

@@ -7,7 +7,8 @@ run against the real oracle (test_oracle_pins.py) and against deliberately
 broken copies of it (test_oracle_mutants.py).
 
 Sources of truth used here, none of which is the oracle's own code:
-  * closed forms of Eq. A (page "Shape-Aware Attention", section "Inspiration"):
+  * closed forms of the attention equation (page "Shape-Aware Attention",
+    section "Inspiration"):
     zero queries give the (prefix) mean of V; a row that sees one key returns
     that key's value row; a dominant one-hot score selects one value row; a
     two-key row is a logistic blend; adding a per-row constant to every score

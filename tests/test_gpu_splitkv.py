@@ -2,7 +2,7 @@
 through the C ABI (needs an MI355X).
 
 attn_fwd_splitkv against the oracle (the split changes only the summation
-order, so the reference is plain Eq. A): decode-like single rows and a few
+order, so the reference is the plain attention equation): decode-like single rows and a few
 rows against long caches, causal and not, bf16/fp16/fp32, range counts from 1
 to more ranges than key tiles (empty ranges), ragged tiles; one range equals
 attn_fwd_chunked bit for bit; graph replays equal eager calls; one workspace

@@ -1,7 +1,7 @@
 """The oracle against its pins (CPU only).
 
 Each check in oracle_pins.py compares the oracle with something that is not the
-oracle: closed forms of Eq. A, exact invariants, torch's float64 SDPA with an
+oracle: closed forms of the attention equation, exact invariants, torch's float64 SDPA with an
 explicit mask, and 50-digit brute force.  The workload-sized checks below run
 the same library special case on the shapes of the five workloads (full
 tensors for the small ones, a few heads of the larger ones)."""

@@ -16,7 +16,8 @@ built, importing this package raises.
 
 q: [B, H, S_q, 64]; k, v: [B, H, S_kv, 64]; all contiguous, same dtype
 (float32, float16 or bfloat16) and same CUDA (HIP) device.  scale=None means
-1/sqrt(64) (Eq. A, page "Shape-Aware Attention", section "Inspiration").
+1/sqrt(64) (the attention equation of page "Shape-Aware Attention", section
+"Inspiration").
 """
 from __future__ import annotations
 

@@ -1,7 +1,7 @@
 // attn_fwd.hip -- fused attention forward for AMD Instinct MI355X (gfx950).
 //
-// O = softmax(Q K^T * scale [+ causal mask]) V  (Eq. A, page "Shape-Aware
-// Attention", section "Inspiration") with online softmax: each query row keeps
+// O = softmax(Q K^T * scale [+ causal mask]) V  (the attention equation of
+// page "Shape-Aware Attention", section "Inspiration") with online softmax: each query row keeps
 // a running maximum m, a running sum l and an fp32 accumulator across key/value
 // blocks, rescaling when the maximum grows (page "GPU Kernel for a Transformer
 // Layer", section "What we learned"), so no [S_q, S_kv] score matrix exists.
