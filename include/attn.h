@@ -274,19 +274,27 @@ int attn_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *
                    int dtype, void *stream);
 
 /*
- * Schedule introspection (host only, no GPU needed).  attn_sched_grid writes the
- * number of workgroups one attn_fwd_chunked call with these sizes launches
- * (attn_fwd: chunk = S_q, kv_len = S_kv; causal as in the call, 0/1);
- * attn_sched_tile writes which head
- * (b*H + h) and which query rows [row0, row1) workgroup `block` computes.
- * Every (head, row) is covered by exactly one workgroup; windows run heaviest
- * first.  Both return ATTN_OK, or ATTN_E_SHAPE for sizes out of range or a
- * NULL output pointer.
+ * Schedule introspection (host only, no GPU needed).
+ *
+ * attn_sched_rows writes the query rows per workgroup (128, or 64) and
+ * whether the keys are split between two wave groups (1 or 2) of an
+ * attn_fwd / attn_fwd_chunked / attn_fwd_varlen launch of these sizes,
+ * causal flag (0/1) and dtype on a device with n_cu compute units (the launch
+ * reads n_cu from the device).  attn_sched_grid writes the number of workgroups one
+ * attn_fwd_chunked call with these sizes launches for `rows` query rows per
+ * workgroup (attn_fwd: chunk = S_q, kv_len = S_kv; causal as in the call,
+ * 0/1); attn_sched_tile writes which head (b*H + h) and which query rows
+ * [row0, row1) workgroup `block` computes.  Every (head, row) is covered by
+ * exactly one workgroup; windows run heaviest first.  All return ATTN_OK, or
+ * ATTN_E_SHAPE for sizes out of range, rows other than 64 and 128, or a NULL
+ * output pointer (attn_sched_rows: ATTN_E_DTYPE for an unknown dtype).
  */
+int attn_sched_rows(int B, int H, int S_q, int causal, int dtype, int n_cu,
+                    int *rows, int *key_split);
 int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal,
-                    int *grid);
+                    int rows, int *grid);
 int attn_sched_tile(int B, int H, int S_q, int chunk, int kv_len, int causal,
-                    int block, int *head, int *row0, int *row1);
+                    int rows, int block, int *head, int *row0, int *row1);
 
 /* Static, NUL-terminated description of an attn_status value (never NULL). */
 const char *attn_strerror(int status);

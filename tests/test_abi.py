@@ -119,23 +119,24 @@ def test_noncausal_allows_more_queries_than_keys():
     assert call(causal=0, S_q=500, kv_len=7) == A.ATTN_E_DEVICE  # passes validation, stops at the device check
 
 
+@pytest.mark.parametrize("rows", [128, 64])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("B,H,S_q,chunk,kv_len", [
     (1, 1, 1, 1, 1), (1, 1, 128, 128, 128), (1, 1, 129, 129, 129), (2, 3, 300, 64, 300), (2, 4, 300, 100, 300),
     (1, 8, 1000, 7, 1000), (4, 8, 2048, 2048, 2048), (8, 8, 512, 512, 512), (3, 5, 777, 256, 777),
     (2, 8, 5000, 4096, 20000), (1, 16, 4096, 1000, 4096), (16, 1, 64, 1, 64), (2, 8, 3000, 1000, 9000),
 ])
-def test_schedule_covers_every_row_once(B, H, S_q, chunk, kv_len, causal):
-    grid = A.sched_grid(B, H, S_q, chunk, kv_len, causal)
+def test_schedule_covers_every_row_once(B, H, S_q, chunk, kv_len, causal, rows):
+    grid = A.sched_grid(B, H, S_q, chunk, kv_len, causal, rows)
     seen = {}
     n_win = -(-S_q // chunk)
     tile_major = causal and kv_len <= 8192
     groups = 8 if (B * H) % 8 == 0 else 1
     seq = {g: [] for g in range(groups)}
     for blk in range(grid):
-        h, r0, r1 = A.sched_tile(B, H, S_q, chunk, blk, kv_len, causal)
+        h, r0, r1 = A.sched_tile(B, H, S_q, chunk, blk, kv_len, causal, rows)
         seq[blk % groups].append((r0 // chunk, r0, h))
-        assert 0 <= h < B * H and 0 <= r0 < r1 <= S_q and r1 - r0 <= 128
+        assert 0 <= h < B * H and 0 <= r0 < r1 <= S_q and r1 - r0 <= rows
         assert r0 // chunk == (r1 - 1) // chunk, "tile straddles a window"
         seen.setdefault(h, []).append((r0, r1))
         if (B * H) % 8 == 0:
@@ -166,6 +167,34 @@ def test_schedule_covers_every_row_once(B, H, S_q, chunk, kv_len, causal):
                     rows = [r0 for r0, h in inside if h == hh]
                     assert rows == sorted(rows, reverse=True)
     assert n_win == len({w for items in seq.values() for w, _, _ in items})
+
+
+def test_launch_shape_rule():
+    """attn_sched_rows: 128-row tiles with one wave group above two 128-row
+    tiles per CU, the keys split between two wave groups at or below it; the
+    16-bit types take 64-row tiles for causal grids below two 128-row tiles
+    per CU and for other grids whose last partial round of 128-row tiles
+    fills at most half the CUs."""
+    for B, H, S_q in ((1, 1, 1), (1, 1, 128), (8, 8, 512), (4, 8, 512), (4, 8, 513), (4, 8, 2048), (4, 8, 2049),
+                      (3, 8, 1024), (8, 8, 768), (5, 8, 1024), (7, 8, 1024), (32, 16, 1024), (16, 16, 98304),
+                      (2, 1, 32768), (2, 1, 32769)):
+        tiles = B * H * -(-S_q // 128)
+        for causal in (False, True):
+            for dt in ("f32", "f16", "bf16"):
+                rows, ks = A.sched_rows(B, H, S_q, causal, dt, 256)
+                assert ks == (2 if tiles <= 512 else 1)
+                fine = ks == 2 and (tiles < 512 if causal else tiles % 256 != 0 and 2 * (tiles % 256) <= 256)
+                assert rows == (64 if fine and dt != "f32" else 128)
+    assert A.sched_rows(4, 8, 2048, True, "bf16", 256) == (128, 2)    # c3: two tiles per CU
+    assert A.sched_rows(8, 8, 512, False, "f16", 256) == (128, 2)     # c2: one tile per CU
+    assert A.sched_rows(4, 8, 1024, True, "bf16", 256) == (64, 2)
+    assert A.sched_rows(8, 8, 768, False, "bf16", 256) == (64, 2)     # 384 tiles: 1.5 per CU
+    assert A.sched_rows(3, 8, 1024, False, "bf16", 256) == (128, 2)   # 192 tiles: 0.75 per CU
+    assert A.sched_rows(4, 8, 2048, True, "bf16", 128) == (128, 1)    # 512 tiles on 128 CUs
+    with pytest.raises(A.AttnError):
+        A.sched_rows(1, 1, 1, True, "bf16", 0)
+    with pytest.raises(A.AttnError):
+        A.sched_grid(1, 1, 128, 128, 128, False, 96)
 
 
 def test_long_context_grid_size():

@@ -32,19 +32,22 @@ LANE = np.arange(64)
 
 
 class Geometry:
-    """Compile-time constants of one kernel instance."""
+    """Compile-time constants of one kernel instance (QG: 32-row query groups
+    per workgroup, 4, or 2 for the 16-bit key split's 64-row tiles)."""
 
-    def __init__(self, esz, KS):
-        self.esz, self.KS = esz, KS
+    def __init__(self, esz, KS, QG=4):
+        self.esz, self.KS, self.QG = esz, KS, QG
         self.ROWB = 64 * esz
         self.TILE = 64 * self.ROWB
         self.STAGE = 2 * KS * self.TILE
         self.NS = 3 if KS == 1 else 2
         self.LPR = self.ROWB // 16
         self.RPC = 64 // self.LPR
-        self.NCP = self.ROWB // 64
-        self.CSTEP = self.RPC * 4 * self.ROWB
-        assert self.CSTEP == 4096 and self.NCP % 2 == 0
+        self.NCP = 64 // (QG * self.RPC)
+        self.CSTEP = self.RPC * QG * self.ROWB
+        assert self.CSTEP in (2048, 4096) and self.NCP % 2 == 0
+        assert QG == 4 or (QG == 2 and KS == 2 and esz == 2)
+        assert QG * KS * 32 * self.ROWB <= self.STAGE   # the Q slabs fit a stage
         sizes = [self.STAGE, self.STAGE, self.STAGE if self.NS == 3 else 16]
         self.stage_base = [0, sizes[0], sizes[0] + sizes[1]]
         self.stage_size = sizes
@@ -60,7 +63,11 @@ class Geometry:
 
     def copy_row(self, i, wave):
         """Stage row of copy i for every lane of `wave` (the current kernel)."""
-        return 64 * (wave >> 2) + self.RPC * (4 * i + (wave & 3)) + LANE // self.LPR
+        QG = self.QG
+        return 64 * (wave // QG) + self.RPC * (QG * i + wave % QG) + LANE // self.LPR
+
+    def wgs_per_cu(self):
+        return 3 if (self.esz == 2 and self.KS == 1) else (2 if self.QG == 2 else 1)
 
 
 class Box:
@@ -87,12 +94,20 @@ def stage_of(j, NS):
 
 
 def launch_params(B, H, S_q, S_kv, causal, esz, chunk=None, kv_len=None, n_split=1, lens=None):
+    """The launch the library makes on a 256-CU device: the split path always
+    takes 128-row tiles with one wave group; otherwise the library's own rule
+    (attn_sched_rows) gives the tile height and the key split."""
     kv_len = S_kv if kv_len is None else kv_len
     chunk = S_q if chunk is None else chunk
-    tiles = B * H * -(-S_q // BM)
-    KS = 1 if n_split > 1 else (2 if tiles <= 2 * N_CU else 1)
+    if n_split > 1:
+        rows, KS = BM, 1
+    else:
+        rows, KS = A.sched_rows(B, H, S_q, causal, "bf16" if esz == 2 else "f32", N_CU)
+        tiles = B * H * -(-S_q // BM)
+        fine = KS == 2 and (tiles < 2 * N_CU if causal else tiles % N_CU != 0 and 2 * (tiles % N_CU) <= N_CU)
+        assert KS == (2 if tiles <= 2 * N_CU else 1) and rows == (64 if fine and esz == 2 else 128)
     return dict(B=B, H=H, S_q=S_q, S_kv=S_kv, causal=causal, esz=esz, chunk=chunk, kv_len=kv_len,
-                n_split=n_split, lens=lens, KS=KS)
+                n_split=n_split, lens=lens, KS=KS, rows=rows, QG=rows // 32)
 
 
 def blocks_to_check(grid, limit=600):
@@ -108,11 +123,11 @@ def blocks_to_check(grid, limit=600):
 def emulate_current(P, box):
     """The current kernel: VGPR 64-bit copy addresses, paired copies, Q slabs,
     epilogue staging and stores, split states."""
-    g = Geometry(P["esz"], P["KS"])
-    assert g.lds_bytes * (3 if (P["esz"] == 2 and P["KS"] == 1) else 1) <= LDS_CU
+    g = Geometry(P["esz"], P["KS"], P["QG"])
+    assert g.lds_bytes * g.wgs_per_cu() <= LDS_CU
     B, H, S_q, S_kv, causal = P["B"], P["H"], P["S_q"], P["S_kv"], P["causal"]
-    ROWB, KS = g.ROWB, P["KS"]
-    base_grid = A.sched_grid(B, H, S_q, P["chunk"] if P["n_split"] == 1 else S_q, P["kv_len"], causal)
+    ROWB, KS, QG, rows_wg = g.ROWB, P["KS"], P["QG"], P["rows"]
+    base_grid = A.sched_grid(B, H, S_q, P["chunk"] if P["n_split"] == 1 else S_q, P["kv_len"], causal, rows_wg)
     n_split = P["n_split"]
     span = 0
     if n_split > 1:
@@ -122,8 +137,9 @@ def emulate_current(P, box):
     head_kv = S_kv * ROWB
     for blk in blocks_to_check(base_grid * n_split):
         split, tile = divmod(blk, base_grid)
-        head, row0, row1 = A.sched_tile(B, H, S_q, P["chunk"] if n_split == 1 else S_q, tile, P["kv_len"], causal)
-        assert 0 <= head < B * H and 0 <= row0 < row1 <= S_q
+        head, row0, row1 = A.sched_tile(B, H, S_q, P["chunk"] if n_split == 1 else S_q, tile, P["kv_len"], causal,
+                                        rows_wg)
+        assert 0 <= head < B * H and 0 <= row0 < row1 <= S_q and row1 - row0 <= rows_wg
         if P["lens"] is not None:
             kv_full = min(max(int(P["lens"][head // H]), 0), S_kv)
         else:
@@ -141,8 +157,8 @@ def emulate_current(P, box):
         kv_lo = head * head_kv
         kv_hi = kv_lo + kv_full * ROWB
         kbase = kv_lo + k_start * ROWB
-        for wave in range(4 * KS):
-            qg, kh = wave & 3, wave >> 2
+        for wave in range(QG * KS):
+            qg, kh = wave % QG, wave // QG
             wrow0 = row0 + 32 * qg
             # Q slab: whole rows, K's swizzle, clamped to the tile's last row,
             # in the stage the first step refills (the last of the NS stages)
@@ -160,7 +176,7 @@ def emulate_current(P, box):
             vc = [g.vswz(r, LANE % g.LPR) for r in rows]
             kof = [u32(r * ROWB + c) for r, c in zip(rows, kc)]
             vof = [u32(r * ROWB + c) for r, c in zip(rows, vc)]
-            for i in range(0, g.NCP, 2):   # a pair shares one address: copy i+1 lies 4096 bytes on
+            for i in range(0, g.NCP, 2):   # a pair shares one address: copy i+1 lies CSTEP bytes on
                 assert (kof[i + 1] - kof[i] == g.CSTEP).all() and (vof[i + 1] - vof[i] == g.CSTEP).all()
             wdst = (64 * kh + g.RPC * qg) * ROWB
             n_full = min(n_super, kv_len // (KS * BN))    # super-tiles wholly below the cache end

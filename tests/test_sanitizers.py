@@ -84,8 +84,8 @@ int main(void) {
       int n = 0, grid = 0, head = 0, r0 = 0, r1 = 0;
       fails += attn_splitkv_choose(B, 16, S < 512 ? S : 1, S, 256, &n) != ATTN_OK;
       fails += attn_splitkv_workspace_bytes(B, 16, S < 512 ? S : 1, n, &bytes) != ATTN_OK;
-      fails += attn_sched_grid(B, 16, S, 4096, S, 1, &grid) != ATTN_OK;
-      fails += attn_sched_tile(B, 16, S, 4096, S, 1, grid - 1, &head, &r0, &r1) != ATTN_OK;
+      fails += attn_sched_grid(B, 16, S, 4096, S, 1, 128, &grid) != ATTN_OK;
+      fails += attn_sched_tile(B, 16, S, 4096, S, 1, 128, grid - 1, &head, &r0, &r1) != ATTN_OK;
       fails += !(r0 < r1 && r1 <= S);
     }
   for (int c = -1; c < 14; ++c) fails += attn_strerror(c) == 0;

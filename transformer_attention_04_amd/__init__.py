@@ -38,8 +38,8 @@ globals().update({name: code for code, name in STATUS.items()})
 NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
 EXPORTS = ("attn_fwd", "attn_fwd_chunked", "attn_fwd_varlen", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc",
            "attn_splitkv_workspace_bytes",
-           "attn_splitkv_choose", "attn_kv_append", "attn_qkv_proj", "attn_strerror", "attn_sched_grid",
-           "attn_sched_tile")
+           "attn_splitkv_choose", "attn_kv_append", "attn_qkv_proj", "attn_strerror", "attn_sched_rows",
+           "attn_sched_grid", "attn_sched_tile")
 
 
 class AttnError(RuntimeError):
@@ -84,9 +84,11 @@ def _load(path: str = LIB_PATH):
     lib.attn_kv_append.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
-    lib.attn_sched_grid.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i)]
+    lib.attn_sched_rows.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.attn_sched_rows.restype = i
+    lib.attn_sched_grid.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
     lib.attn_sched_grid.restype = i
-    lib.attn_sched_tile.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.attn_sched_tile.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.attn_sched_tile.restype = i
     return lib
 
@@ -365,18 +367,31 @@ fwd = attn_fwd
 fwd_chunked = attn_fwd_chunked
 
 
-def sched_grid(B: int, H: int, S_q: int, chunk: int, kv_len: int | None = None, causal: bool = True) -> int:
+def sched_rows(B: int, H: int, S_q: int, causal: bool, dtype: str, n_cu: int = 256):
+    """(query rows per workgroup, key split 1 or 2) of an attn_fwd launch of
+    these sizes on a device with n_cu compute units."""
+    r, ks = ctypes.c_int(), ctypes.c_int()
+    st = lib.attn_sched_rows(B, H, S_q, int(bool(causal)), {"f32": ATTN_F32, "f16": ATTN_F16, "bf16": ATTN_BF16}[dtype],
+                             n_cu, ctypes.byref(r), ctypes.byref(ks))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return r.value, ks.value
+
+
+def sched_grid(B: int, H: int, S_q: int, chunk: int, kv_len: int | None = None, causal: bool = True,
+               rows: int = 128) -> int:
     g = ctypes.c_int()
-    st = lib.attn_sched_grid(B, H, S_q, chunk, S_q if kv_len is None else kv_len, int(bool(causal)), ctypes.byref(g))
+    st = lib.attn_sched_grid(B, H, S_q, chunk, S_q if kv_len is None else kv_len, int(bool(causal)), rows,
+                             ctypes.byref(g))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
     return g.value
 
 
 def sched_tile(B: int, H: int, S_q: int, chunk: int, block: int, kv_len: int | None = None,
-               causal: bool = True):
+               causal: bool = True, rows: int = 128):
     h, r0, r1 = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    st = lib.attn_sched_tile(B, H, S_q, chunk, S_q if kv_len is None else kv_len, int(bool(causal)), block,
+    st = lib.attn_sched_tile(B, H, S_q, chunk, S_q if kv_len is None else kv_len, int(bool(causal)), rows, block,
                              ctypes.byref(h), ctypes.byref(r0), ctypes.byref(r1))
     if st != 0:
         raise AttnError(st, attn_strerror(st))

@@ -86,6 +86,7 @@ constexpr float ROW_LIMIT = 65536.0f;  // largest 64-key row sum (16-bit paths) 
 constexpr int TILE_MAJOR_MAX_KV = 8192;  // cache rows up to which causal windows go tile-major
 
 struct Sched {
+  int bm;          // query rows per workgroup (128, or 64 for the 16-bit key split)
   int S_q;
   int chunk;       // rows per window
   int n_win;       // windows
@@ -128,8 +129,8 @@ __host__ __device__ inline void decode_tile(const Sched& s, int b, int& head, in
   head = j * s.groups + grp;
   const int wstart = w * s.chunk;
   const int wend = min(s.S_q, wstart + s.chunk);
-  row0 = wstart + t * BM;
-  row1 = min(wend, row0 + BM);
+  row0 = wstart + t * s.bm;
+  row1 = min(wend, row0 + s.bm);
 }
 
 template <typename T>
@@ -547,9 +548,12 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 // cache) and writes the partial (m, l, acc) instead of O.
 // Occupancy: three four-wave 16-bit workgroups per CU (48 KB of LDS and at
 // most 168 VGPRs each), else one or two.
-template <typename T, bool CAUSAL, int KS, bool VARLEN, bool SPLIT>
-__global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3 : 1)
+template <typename T, bool CAUSAL, int KS, bool VARLEN, bool SPLIT, int QG = 4>
+__global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 : (QG == 2 ? 2 : 1))
     attn_fwd_kernel(Params<T> p) {
+  // QG: 32-row query groups per workgroup (4: 128 rows; 2: 64 rows, 16-bit
+  // key split only, two four-wave workgroups per CU).
+  static_assert(QG == 4 || (QG == 2 && KS == 2 && sizeof(T) == 2), "64-row tiles: 16-bit key split only");
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ROWB = F32 ? 256 : 128;  // bytes per K/V row (64 elements)
   constexpr int TILE = 64 * ROWB;        // one 64-row tile of K or V
@@ -557,7 +561,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   constexpr int NS = KS == 1 ? 3 : 2;    // LDS stages
   constexpr int LPR = ROWB / 16;         // lanes per row in one 16-byte-per-lane copy
   constexpr int RPC = 64 / LPR;          // rows per copy instruction
-  constexpr int NCP = ROWB / 64;         // copies per wave per matrix per stage
+  constexpr int NCP = 64 / (QG * RPC);   // copies per wave per matrix per stage
   // Distinct arrays: reading one stage never waits for copies into another.
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
@@ -578,8 +582,8 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // as exec-masked branches they stay in place.
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int qg = wave & 3;    // query group: rows 32*qg .. +31 of the tile
-  const int kh = wave >> 2;   // key half (KS = 2)
+  const int qg = wave % QG;   // query group: rows 32*qg .. +31 of the tile
+  const int kh = wave / QG;   // key half (KS = 2)
   const int c = lane & 31;    // query column of the S^T / O^T tiles
   const int hf = lane >> 5;   // half-wave
 
@@ -615,11 +619,11 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   typename std::conditional<F32, float[32], typename Half16<typename std::conditional<F32, __bf16, T>::type>::vec8[4]>::type qop;
 
   // Tile copies: the waves of key half kh copy its 64-row tile of K and of V;
-  // copy i of wave (kh, qg) fills stage rows 64 kh + RPC*(4i + qg) .. +RPC-1,
+  // copy i of wave (kh, qg) fills stage rows 64 kh + RPC*(QG i + qg) .. +RPC-1,
   // lane l lands in row + l/LPR, physical chunk l%LPR and fetches the logical
   // chunk the row's swizzle maps there.  The swizzle depends only on the low
   // bits of the row, equal for all copies of a wave, so copy i + 1 lies
-  // 4 RPC rows = 4096 bytes after copy i in the source and in the stage.  The
+  // QG RPC rows = CSTEP bytes after copy i in the source and in the stage.  The
   // source is a per-lane address fixed for the whole loop, advanced by the
   // super-tile's (scalar) offset; only a super-tile that crosses the cache
   // end computes clamped rows (rows past kv_len - 1 re-read row kv_len - 1:
@@ -630,7 +634,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // of them stays live across the key loop.
   auto copy_geom = [&](const int i, const int t, int& row, uint32_t& kc, uint32_t& vc) __attribute__((always_inline)) {
     const int ln = t & 63, wv = t >> 6;
-    row = 64 * (wv >> 2) + RPC * (4 * i + (wv & 3)) + ln / LPR;
+    row = 64 * (wv / QG) + RPC * (QG * i + (wv % QG)) + ln / LPR;
     const int ph = ln % LPR;
     if constexpr (F32) {
       kc = 16 * (ph ^ (row & 15));
@@ -660,17 +664,18 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
     vl[i] = vbase + vof[i];
   }
   // A super-tile entirely below the cache end.
-  // Copy i + 1 lies CSTEP = 4096 bytes after copy i in the source and in the
-  // stage: consecutive copies go in pairs (dma16_pair).
-  constexpr int CSTEP = RPC * 4 * ROWB;
-  static_assert(CSTEP == 4096 && NCP % 2 == 0, "paired tile copies");
+  // Copy i + 1 lies CSTEP bytes (4096, or 2048 with 64-row tiles) after copy
+  // i in the source and in the stage: consecutive copies go in pairs
+  // (dma16_pair, offsets -CSTEP/2 and +CSTEP/2 around one address).
+  constexpr int CSTEP = RPC * QG * ROWB;
+  static_assert((CSTEP == 4096 || CSTEP == 2048) && NCP % 2 == 0, "paired tile copies");
   auto issue_full = [&](char* st, int super) __attribute__((always_inline)) {
     const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     const int64_t off = (int64_t)super * KS * BN * ROWB;
 #pragma unroll
     for (int i = 0; i < NCP; i += 2) {
-      dma16_pair(kl[i] + (off + 2048), mk + i * CSTEP + 2048);
-      dma16_pair(vl[i] + (off + 2048), mv + i * CSTEP + 2048);
+      dma16_pair<CSTEP / 2>(kl[i] + (off + CSTEP / 2), mk + i * CSTEP + CSTEP / 2);
+      dma16_pair<CSTEP / 2>(vl[i] + (off + CSTEP / 2), mv + i * CSTEP + CSTEP / 2);
     }
   };
   auto issue = [&](char* st, int super) __attribute__((always_inline)) {
@@ -700,7 +705,8 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
   // before that step's barrier.  Whole-row copies instead of per-lane loads
   // that touch 32 rows each, and the first step waits only for what it needs.
   // Rows past the tile's end re-read its last row (never stored).
-  constexpr int SLAB = 32 * ROWB;  // one wave's Q rows; 4 KS slabs fit in a stage
+  constexpr int SLAB = 32 * ROWB;  // one wave's Q rows; the QG KS slabs fit in a stage
+  static_assert(QG * KS * SLAB <= STAGE, "Q slabs");
   char* const qst = NS == 3 ? st2 : st1;
   const uint32_t wslab = __builtin_amdgcn_readfirstlane((uint32_t)(wave * SLAB));
   {
@@ -1055,7 +1061,7 @@ __global__ void __launch_bounds__(NTHREADS * KS, (sizeof(T) == 2 && KS == 1) ? 3
     const int os = (n_super + 1) % 3;
     ot = (os == 0 ? st0 : os == 1 ? st1 : st2) + (tx >> 6) * (32 * ROWB);
   } else {
-    ot = st0 + ((tx >> 6) & 3) * (8 * 64 * 16);
+    ot = st0 + ((tx >> 6) % QG) * (8 * 64 * 16);
   }
   if constexpr (F32) {
     // acc[dt] row i = 8(r/4) + 4hf + r%4 is column d = 2i + dt: registers
@@ -1213,37 +1219,59 @@ int validate(const void* q, const void* k, const void* v, void* o, int B, int H,
   return ATTN_OK;
 }
 
-Sched make_sched(int B, int H, int S_q, int chunk, int kv_len, int causal) {
+Sched make_sched(int B, int H, int S_q, int chunk, int kv_len, int causal, int bm) {
   Sched s;
+  s.bm = bm;
   s.tile_major = causal && kv_len <= TILE_MAJOR_MAX_KV;
   s.S_q = S_q;
   s.chunk = std::min(chunk, S_q);
   s.n_win = (S_q + s.chunk - 1) / s.chunk;
-  s.tf = (s.chunk + BM - 1) / BM;
+  s.tf = (s.chunk + bm - 1) / bm;
   const int last_rows = S_q - (s.n_win - 1) * s.chunk;
-  s.tl = (last_rows + BM - 1) / BM;
+  s.tl = (last_rows + bm - 1) / bm;
   const int bh = B * H;
   s.groups = (bh % 8 == 0) ? 8 : 1;
   s.heads = bh / s.groups;
   return s;
 }
 
-template <typename T, int KS, bool VARLEN, bool SPLIT>
+template <typename T, int KS, bool VARLEN, bool SPLIT, int QG>
 void launch_kernel_v(const Params<T>& p, int grid, int causal, hipStream_t stream) {
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS, VARLEN, SPLIT>), dim3(grid), dim3(NTHREADS * KS), 0, stream,
-                       p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, true, KS, VARLEN, SPLIT, QG>), dim3(grid), dim3(64 * QG * KS), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS, VARLEN, SPLIT>), dim3(grid), dim3(NTHREADS * KS), 0, stream,
-                       p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, false, KS, VARLEN, SPLIT, QG>), dim3(grid), dim3(64 * QG * KS), 0,
+                       stream, p);
 }
 
-template <typename T, int KS>
+template <typename T, int KS, int QG = 4>
 void launch_kernel(const Params<T>& p, int grid, int causal, hipStream_t stream) {
   if (p.kv_lens)
-    launch_kernel_v<T, KS, true, false>(p, grid, causal, stream);
+    launch_kernel_v<T, KS, true, false, QG>(p, grid, causal, stream);
   else
-    launch_kernel_v<T, KS, false, false>(p, grid, causal, stream);
+    launch_kernel_v<T, KS, false, false, QG>(p, grid, causal, stream);
+}
+
+// Query rows per workgroup of an attn_fwd / attn_fwd_chunked / attn_fwd_varlen
+// launch, and whether the keys are split between two wave groups.  Few
+// 128-row query tiles (at most two per CU): split each tile's key range
+// between two wave groups so every SIMD runs two waves on half the key chain.
+// 16-bit types then take 64-row tiles (four waves: 2 query groups x 2 key
+// halves, two workgroups per CU) where the finer grain balances the CUs:
+// causal grids below two 128-row tiles per CU (their tiles differ in length),
+// and other grids whose last round of 128-row tiles would fill at most half
+// the CUs.  Elsewhere a CU running two 64-row workgroups is slower than one
+// eight-wave workgroup on the same rows (each loads all K/V for half the
+// rows).  The choice depends on B, H, S_q, causal, the type and the CU count
+// only, never on the window size, so chunked and unchunked calls sum in the
+// same order.
+void launch_shape(int B, int H, int S_q, int causal, int dtype, int n_cu, int& rows, int& ks) {
+  const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
+  ks = tiles <= 2 * (int64_t)n_cu ? 2 : 1;
+  const int64_t last = tiles % n_cu;  // 128-row tiles in a last, partial round
+  const bool fine = ks == 2 && (causal ? tiles < 2 * (int64_t)n_cu : last != 0 && 2 * last <= (int64_t)n_cu);
+  rows = (dtype != ATTN_F32 && fine) ? 64 : BM;
 }
 
 template <typename T>
@@ -1271,7 +1299,9 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   // exp2(~1e-27) = 1 exactly in fp32.
   p.c = (float)std::max(std::fabs((double)scale) * 1.4426950408889634, 1e-30);
   p.q_flip = (scale < 0.f) ? (sizeof(T) == 4 ? 0x80000000u : 0x80008000u) : 0u;
-  p.s = make_sched(B, H, S_q, chunk, kv_len, causal);
+  int rows = BM, ks = 1;
+  if (n_split == 1) launch_shape(B, H, S_q, causal, sizeof(T) == 4 ? ATTN_F32 : ATTN_BF16, n_cu, rows, ks);
+  p.s = make_sched(B, H, S_q, chunk, kv_len, causal, rows);
   const int grid = p.s.groups * p.s.heads * (p.s.tl + (p.s.n_win - 1) * p.s.tf);
   p.base_grid = grid;
   if (n_split > 1) {
@@ -1297,15 +1327,12 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
                        p.ws_acc, p.ws_ml, static_cast<T*>(o), rows, n_split);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
   }
-  // Few 128-row query tiles (at most two per CU): split each tile's key range
-  // between two wave groups so every SIMD runs two waves on half the key
-  // chain.  The choice depends on B, H and S_q only, never on the window
-  // size, so chunked and unchunked calls sum in the same order.
-  const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
-  if (tiles <= 2 * (int64_t)n_cu)
-    launch_kernel<T, 2>(p, grid, causal, stream);
-  else
+  if (ks == 1)
     launch_kernel<T, 1>(p, grid, causal, stream);
+  else if constexpr (sizeof(T) == 2)
+    rows == 64 ? launch_kernel<T, 2, 2>(p, grid, causal, stream) : launch_kernel<T, 2>(p, grid, causal, stream);
+  else
+    launch_kernel<T, 2>(p, grid, causal, stream);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
@@ -1460,7 +1487,7 @@ int splitkv_impl(const void* q, const void* k, const void* v, void* o, int B, in
   size_t need = 0;
   const int ws = attn_splitkv_workspace_bytes(B, H, S_q, n_split, &need);
   if (ws != ATTN_OK) return ws;
-  const Sched sc = make_sched(B, H, S_q, S_q, kv_len, causal);
+  const Sched sc = make_sched(B, H, S_q, S_q, kv_len, causal, BM);
   const int64_t grid = (int64_t)sc.groups * sc.heads * sc.tl;
   const int64_t rows = (int64_t)B * H * S_q;
   if (grid * n_split > INT32_MAX || (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS > INT32_MAX) return ATTN_E_SPLIT;
@@ -1511,24 +1538,33 @@ extern "C" int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void
                       true);
 }
 
-extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int* grid) {
+extern "C" int attn_sched_rows(int B, int H, int S_q, int causal, int dtype, int n_cu, int* rows,
+                               int* key_split) {
+  if (B < 1 || H < 1 || S_q < 1 || n_cu < 1 || !rows || !key_split) return ATTN_E_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  launch_shape(B, H, S_q, causal, dtype, n_cu, *rows, *key_split);
+  return ATTN_OK;
+}
+
+extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int rows, int* grid) {
   if (B < 1 || H < 1 || S_q < 1 || chunk < 1 || kv_len < 1 || !grid) return ATTN_E_SHAPE;
+  if (rows != 64 && rows != BM) return ATTN_E_SHAPE;
   const int64_t bh = (int64_t)B * H;
   const int64_t n_win = ((int64_t)S_q + chunk - 1) / chunk;
-  const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + BM - 1) / BM);
+  const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + rows - 1) / rows);
   if (bh > (int64_t)INT32_MAX || tiles * bh > (int64_t)INT32_MAX) return ATTN_E_SHAPE;
-  const Sched s = make_sched(B, H, S_q, chunk, kv_len, causal);
+  const Sched s = make_sched(B, H, S_q, chunk, kv_len, causal, rows);
   *grid = s.groups * s.heads * (s.tl + (s.n_win - 1) * s.tf);
   return ATTN_OK;
 }
 
-extern "C" int attn_sched_tile(int B, int H, int S_q, int chunk, int kv_len, int causal, int block, int* head,
-                               int* row0, int* row1) {
+extern "C" int attn_sched_tile(int B, int H, int S_q, int chunk, int kv_len, int causal, int rows, int block,
+                               int* head, int* row0, int* row1) {
   int grid = 0;
-  const int st = attn_sched_grid(B, H, S_q, chunk, kv_len, causal, &grid);
+  const int st = attn_sched_grid(B, H, S_q, chunk, kv_len, causal, rows, &grid);
   if (st != ATTN_OK) return st;
   if (block < 0 || block >= grid || !head || !row0 || !row1) return ATTN_E_SHAPE;
-  decode_tile(make_sched(B, H, S_q, chunk, kv_len, causal), block, *head, *row0, *row1);
+  decode_tile(make_sched(B, H, S_q, chunk, kv_len, causal, rows), block, *head, *row0, *row1);
   return ATTN_OK;
 }
 

@@ -37,15 +37,25 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
 
-// Two copies whose sources and destinations both lie 4096 bytes apart, from
-// one address and one M0 at their midpoint: the instruction offset (13-bit
-// signed) applies to the global and the LDS address alike, so the copies
-// take offsets -2048 and +2048.  Same operand rules as dma16.
+// Two copies whose sources and destinations both lie 2 * HALF bytes apart,
+// from one address and one M0 at their midpoint: the instruction offset
+// (13-bit signed) applies to the global and the LDS address alike, so the
+// copies take offsets -HALF and +HALF.  Same operand rules as dma16.
+template <int HALF = 2048>
 __device__ __forceinline__ void dma16_pair(const void* gmid, uint32_t m0mid) {
-  asm volatile(
-      "s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:-2048\n\tglobal_load_lds_dwordx4 %0, off offset:2048" ::"v"(gmid),
-      "{m0}"(m0mid)
-      : "memory");
+  static_assert(HALF == 1024 || HALF == 2048, "offsets within the 13-bit signed field");
+  if constexpr (HALF == 2048)
+    asm volatile(
+        "s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:-2048\n\tglobal_load_lds_dwordx4 %0, off offset:2048" ::"v"(
+            gmid),
+        "{m0}"(m0mid)
+        : "memory");
+  else
+    asm volatile(
+        "s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:-1024\n\tglobal_load_lds_dwordx4 %0, off offset:1024" ::"v"(
+            gmid),
+        "{m0}"(m0mid)
+        : "memory");
 }
 
 // LDS byte address of a __shared__ location (what M0 takes).
