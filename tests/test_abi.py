@@ -174,7 +174,8 @@ def test_launch_shape_rule():
     tiles per CU, the keys split between two wave groups at or below it; the
     16-bit types take 64-row tiles for causal grids below two 128-row tiles
     per CU and for other grids whose last partial round of 128-row tiles
-    fills at most half the CUs."""
+    fills at most half the CUs; fp32 while 64-row tiles still give each
+    workgroup its own CU."""
     for B, H, S_q in ((1, 1, 1), (1, 1, 128), (8, 8, 512), (4, 8, 512), (4, 8, 513), (4, 8, 2048), (4, 8, 2049),
                       (3, 8, 1024), (8, 8, 768), (5, 8, 1024), (7, 8, 1024), (32, 16, 1024), (16, 16, 98304),
                       (2, 1, 32768), (2, 1, 32769)):
@@ -183,10 +184,15 @@ def test_launch_shape_rule():
             for dt in ("f32", "f16", "bf16"):
                 rows, ks = A.sched_rows(B, H, S_q, causal, dt, 256)
                 assert ks == (2 if tiles <= 512 else 1)
-                fine = ks == 2 and (tiles < 512 if causal else tiles % 256 != 0 and 2 * (tiles % 256) <= 256)
-                assert rows == (64 if fine and dt != "f32" else 128)
+                if dt == "f32":
+                    fine = 2 * tiles <= 256
+                else:
+                    fine = ks == 2 and (tiles < 512 if causal else tiles % 256 != 0 and 2 * (tiles % 256) <= 256)
+                assert rows == (64 if fine else 128)
     assert A.sched_rows(4, 8, 2048, True, "bf16", 256) == (128, 2)    # c3: two tiles per CU
     assert A.sched_rows(8, 8, 512, False, "f16", 256) == (128, 2)     # c2: one tile per CU
+    assert A.sched_rows(8, 8, 512, False, "f32", 256) == (128, 2)
+    assert A.sched_rows(1, 1, 128, False, "f32", 256) == (64, 2)      # c1: one tile
     assert A.sched_rows(4, 8, 1024, True, "bf16", 256) == (64, 2)
     assert A.sched_rows(8, 8, 768, False, "bf16", 256) == (64, 2)     # 384 tiles: 1.5 per CU
     assert A.sched_rows(3, 8, 1024, False, "bf16", 256) == (128, 2)   # 192 tiles: 0.75 per CU

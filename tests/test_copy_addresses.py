@@ -45,8 +45,11 @@ class Geometry:
         self.RPC = 64 // self.LPR
         self.NCP = 64 // (QG * self.RPC)
         self.CSTEP = self.RPC * QG * self.ROWB
-        assert self.CSTEP in (2048, 4096) and self.NCP % 2 == 0
-        assert QG == 4 or (QG == 2 and KS == 2 and esz == 2)
+        # copies PG apart (rows a multiple of the 16-row swizzle period apart) go in pairs
+        self.PG = 1 if (QG * self.RPC) % 16 == 0 else 16 // (QG * self.RPC)
+        self.PSTEP = self.PG * self.CSTEP
+        assert self.PSTEP in (2048, 4096) and self.NCP % (2 * self.PG) == 0
+        assert QG == 4 or (QG == 2 and KS == 2)
         assert QG * KS * 32 * self.ROWB <= self.STAGE   # the Q slabs fit a stage
         sizes = [self.STAGE, self.STAGE, self.STAGE if self.NS == 3 else 16]
         self.stage_base = [0, sizes[0], sizes[0] + sizes[1]]
@@ -67,7 +70,7 @@ class Geometry:
         return 64 * (wave // QG) + self.RPC * (QG * i + wave % QG) + LANE // self.LPR
 
     def wgs_per_cu(self):
-        return 3 if (self.esz == 2 and self.KS == 1) else (2 if self.QG == 2 else 1)
+        return 3 if (self.esz == 2 and self.KS == 1) else (2 if (self.QG == 2 and self.esz == 2) else 1)
 
 
 class Box:
@@ -104,8 +107,11 @@ def launch_params(B, H, S_q, S_kv, causal, esz, chunk=None, kv_len=None, n_split
     else:
         rows, KS = A.sched_rows(B, H, S_q, causal, "bf16" if esz == 2 else "f32", N_CU)
         tiles = B * H * -(-S_q // BM)
-        fine = KS == 2 and (tiles < 2 * N_CU if causal else tiles % N_CU != 0 and 2 * (tiles % N_CU) <= N_CU)
-        assert KS == (2 if tiles <= 2 * N_CU else 1) and rows == (64 if fine and esz == 2 else 128)
+        if esz == 4:
+            fine = 2 * tiles <= N_CU
+        else:
+            fine = KS == 2 and (tiles < 2 * N_CU if causal else tiles % N_CU != 0 and 2 * (tiles % N_CU) <= N_CU)
+        assert KS == (2 if tiles <= 2 * N_CU else 1) and rows == (64 if fine else 128)
     return dict(B=B, H=H, S_q=S_q, S_kv=S_kv, causal=causal, esz=esz, chunk=chunk, kv_len=kv_len,
                 n_split=n_split, lens=lens, KS=KS, rows=rows, QG=rows // 32)
 
@@ -176,8 +182,12 @@ def emulate_current(P, box):
             vc = [g.vswz(r, LANE % g.LPR) for r in rows]
             kof = [u32(r * ROWB + c) for r, c in zip(rows, kc)]
             vof = [u32(r * ROWB + c) for r, c in zip(rows, vc)]
-            for i in range(0, g.NCP, 2):   # a pair shares one address: copy i+1 lies CSTEP bytes on
-                assert (kof[i + 1] - kof[i] == g.CSTEP).all() and (vof[i + 1] - vof[i] == g.CSTEP).all()
+            for i in range(g.NCP):   # a pair shares one address: copy i+PG lies PSTEP bytes on
+                if (i // g.PG) % 2 == 0:
+                    j = i + g.PG
+                    assert (kof[j] - kof[i] == g.PSTEP).all() and (vof[j] - vof[i] == g.PSTEP).all()
+                    # and the stage rows are the same distance apart
+                    assert ((rows[j] - rows[i]) * ROWB == g.PSTEP).all()
             wdst = (64 * kh + g.RPC * qg) * ROWB
             n_full = min(n_super, kv_len // (KS * BN))    # super-tiles wholly below the cache end
             full_supers = [0, n_full - 1] if n_full > 0 else []

@@ -42,9 +42,10 @@ def _inputs(B, H, S_q, S_kv, dtype, seed):
     return q.to(t), k.to(t), v.to(t)
 
 
-GRIDS = [  # (B, H, S, what): 36 query tiles split keys between two wave groups; 576 do not
-    (1, 4, 1100, "two wave groups"),
-    (8, 8, 1100, "one wave group"),
+GRIDS = [  # (B, H, S, what), in 128-row query tiles on 256 CUs (A.sched_rows gives the launch's choice):
+    (1, 4, 1100, "two wave groups, 64-row tiles (16-bit)"),           # 36 tiles
+    (4, 8, 2048, "two wave groups, 128-row tiles"),                   # 512 tiles: two per CU
+    (8, 8, 1100, "one wave group"),                                   # 576 tiles
 ]
 
 
@@ -56,7 +57,8 @@ def test_forced_rescale_matches_oracle(dtype):
         assert torch.equal(q.float(), W.rescale_inputs(B, H, S, S, 31)[0])  # exact in the storage type
         qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
         for causal in (False, True):
-            say(f"[rescale] {dtype} {what} B{B} H{H} S{S} causal={causal}")
+            rows, ks = A.sched_rows(B, H, S, causal, dtype, torch.cuda.get_device_properties(0).multi_processor_count)
+            say(f"[rescale] {dtype} {what} B{B} H{H} S{S} causal={causal}: {rows}-row tiles, key split {ks}")
             ref = oracle.attention(q, k, v, causal=causal, scale=SCALE)
             o = A.attn_fwd(qd, kd, vd, causal=causal, scale=SCALE)
             torch.cuda.synchronize()

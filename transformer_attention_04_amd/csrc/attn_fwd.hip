@@ -13,10 +13,13 @@
 //
 // Work decomposition (both element types)
 //   workgroup = 4 wavefronts x 32 query rows = BM = 128 rows of one (b, h);
-//   per iteration the workgroup stages BN = 64 keys of K and V in LDS
-//   (direct global-to-LDS copies, 16 bytes per lane, into three stages issued
-//   two tiles ahead -- two stages, one ahead, when two wave groups split the
-//   keys);
+//   small grids split each tile's keys between two such wave groups (eight
+//   wavefronts), or, for 16-bit types where that leaves CUs unbalanced, take
+//   64-row tiles of 2 query groups x 2 key halves (four wavefronts, two
+//   workgroups per CU); per iteration a wave group stages BN = 64 keys of K
+//   and V in LDS (direct global-to-LDS copies, 16 bytes per lane, into three
+//   stages issued two tiles ahead -- two stages, one ahead, with the key
+//   split);
 //   each wave computes S^T = K Q^T on MFMA so that a lane owns ONE query row
 //   (lane % 32) and 16 keys per 32-key block: the row max and row sum are
 //   in-lane plus one exchange between the two half-waves (v_permlane32_swap);
@@ -549,11 +552,11 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 // Occupancy: three four-wave 16-bit workgroups per CU (48 KB of LDS and at
 // most 168 VGPRs each), else one or two.
 template <typename T, bool CAUSAL, int KS, bool VARLEN, bool SPLIT, int QG = 4>
-__global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 : (QG == 2 ? 2 : 1))
+__global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 : (QG == 2 && sizeof(T) == 2 ? 2 : 1))
     attn_fwd_kernel(Params<T> p) {
-  // QG: 32-row query groups per workgroup (4: 128 rows; 2: 64 rows, 16-bit
-  // key split only, two four-wave workgroups per CU).
-  static_assert(QG == 4 || (QG == 2 && KS == 2 && sizeof(T) == 2), "64-row tiles: 16-bit key split only");
+  // QG: 32-row query groups per workgroup (4: 128 rows; 2: 64 rows, key split
+  // only: four waves, two workgroups per CU for 16-bit types, one for fp32).
+  static_assert(QG == 4 || (QG == 2 && KS == 2), "64-row tiles: key split only");
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ROWB = F32 ? 256 : 128;  // bytes per K/V row (64 elements)
   constexpr int TILE = 64 * ROWB;        // one 64-row tile of K or V
@@ -664,18 +667,24 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
     vl[i] = vbase + vof[i];
   }
   // A super-tile entirely below the cache end.
-  // Copy i + 1 lies CSTEP bytes (4096, or 2048 with 64-row tiles) after copy
-  // i in the source and in the stage: consecutive copies go in pairs
-  // (dma16_pair, offsets -CSTEP/2 and +CSTEP/2 around one address).
+  // Copy i + 1 lies QG RPC rows = CSTEP bytes after copy i in the stage.
+  // Copies PG apart, whose rows differ by a multiple of the swizzle period
+  // (16 rows), also lie PG CSTEP bytes apart in the source: they go in pairs
+  // (dma16_pair, offsets -PG CSTEP/2 and +PG CSTEP/2 around one address).
+  // PG = 1 except for fp32 with 64-row tiles (copies 8 rows apart: pairs
+  // (i, i + 2)).
   constexpr int CSTEP = RPC * QG * ROWB;
-  static_assert((CSTEP == 4096 || CSTEP == 2048) && NCP % 2 == 0, "paired tile copies");
+  constexpr int PG = (QG * RPC) % 16 == 0 ? 1 : 16 / (QG * RPC);
+  constexpr int PSTEP = PG * CSTEP;
+  static_assert((PSTEP == 4096 || PSTEP == 2048) && NCP % (2 * PG) == 0, "paired tile copies");
   auto issue_full = [&](char* st, int super) __attribute__((always_inline)) {
     const uint32_t mk = lds_addr(st) + wdst, mv = mk + KS * TILE;
     const int64_t off = (int64_t)super * KS * BN * ROWB;
 #pragma unroll
-    for (int i = 0; i < NCP; i += 2) {
-      dma16_pair<CSTEP / 2>(kl[i] + (off + CSTEP / 2), mk + i * CSTEP + CSTEP / 2);
-      dma16_pair<CSTEP / 2>(vl[i] + (off + CSTEP / 2), mv + i * CSTEP + CSTEP / 2);
+    for (int i = 0; i < NCP; ++i) {
+      if ((i / PG) % 2 != 0) continue;  // the second copy of a pair
+      dma16_pair<PSTEP / 2>(kl[i] + (off + PSTEP / 2), mk + i * CSTEP + PSTEP / 2);
+      dma16_pair<PSTEP / 2>(vl[i] + (off + PSTEP / 2), mv + i * CSTEP + PSTEP / 2);
     }
   };
   auto issue = [&](char* st, int super) __attribute__((always_inline)) {
@@ -821,10 +830,14 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
   if (n_super > 0) issue(st0, 0);
   if (NS == 3 && n_super > 1) issue(st1, 1);
   // The Q rows and super-tile 0 (copied before super-tile 1).
-  if (NS == 3 && n_super > 1)
-    wait_vmem<2 * NCP>();
-  else
+  if constexpr (NS == 3) {
+    if (n_super > 1)
+      wait_vmem<2 * NCP>();
+    else
+      wait_vmem<0>();
+  } else {
     wait_vmem<0>();
+  }
   read_q();
 
   int j = 0;
@@ -1263,15 +1276,19 @@ void launch_kernel(const Params<T>& p, int grid, int causal, hipStream_t stream)
 // and other grids whose last round of 128-row tiles would fill at most half
 // the CUs.  Elsewhere a CU running two 64-row workgroups is slower than one
 // eight-wave workgroup on the same rows (each loads all K/V for half the
-// rows).  The choice depends on B, H, S_q, causal, the type and the CU count
-// only, never on the window size, so chunked and unchunked calls sum in the
-// same order.
+// rows).  fp32 takes them only while the 64-row grid still gives every
+// workgroup a CU of its own (its two LDS stages fill 128 KB): each SIMD then
+// runs one wave instead of two.  The choice depends on B, H, S_q, causal, the
+// type and the CU count only, never on the window size, so chunked and
+// unchunked calls sum in the same order.
 void launch_shape(int B, int H, int S_q, int causal, int dtype, int n_cu, int& rows, int& ks) {
   const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
   ks = tiles <= 2 * (int64_t)n_cu ? 2 : 1;
   const int64_t last = tiles % n_cu;  // 128-row tiles in a last, partial round
-  const bool fine = ks == 2 && (causal ? tiles < 2 * (int64_t)n_cu : last != 0 && 2 * last <= (int64_t)n_cu);
-  rows = (dtype != ATTN_F32 && fine) ? 64 : BM;
+  const bool fine = dtype == ATTN_F32 ? 2 * tiles <= (int64_t)n_cu
+                                      : ks == 2 && (causal ? tiles < 2 * (int64_t)n_cu
+                                                           : last != 0 && 2 * last <= (int64_t)n_cu);
+  rows = fine ? 64 : BM;
 }
 
 template <typename T>
@@ -1329,8 +1346,8 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   }
   if (ks == 1)
     launch_kernel<T, 1>(p, grid, causal, stream);
-  else if constexpr (sizeof(T) == 2)
-    rows == 64 ? launch_kernel<T, 2, 2>(p, grid, causal, stream) : launch_kernel<T, 2>(p, grid, causal, stream);
+  else if (rows == 64)
+    launch_kernel<T, 2, 2>(p, grid, causal, stream);
   else
     launch_kernel<T, 2>(p, grid, causal, stream);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
