@@ -89,7 +89,7 @@ constexpr float ROW_LIMIT = 65536.0f;  // largest 64-key row sum (16-bit paths) 
 constexpr int TILE_MAJOR_MAX_KV = 8192;  // cache rows up to which causal windows go tile-major
 
 struct Sched {
-  int bm;          // query rows per workgroup (128, or 64 for the 16-bit key split)
+  int bm;          // query rows per workgroup (128, or 64 for the key split on small grids)
   int S_q;
   int chunk;       // rows per window
   int n_win;       // windows
@@ -624,9 +624,9 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
   // Tile copies: the waves of key half kh copy its 64-row tile of K and of V;
   // copy i of wave (kh, qg) fills stage rows 64 kh + RPC*(QG i + qg) .. +RPC-1,
   // lane l lands in row + l/LPR, physical chunk l%LPR and fetches the logical
-  // chunk the row's swizzle maps there.  The swizzle depends only on the low
-  // bits of the row, equal for all copies of a wave, so copy i + 1 lies
-  // QG RPC rows = CSTEP bytes after copy i in the source and in the stage.  The
+  // chunk the row's swizzle maps there.  The swizzle depends only on the row
+  // modulo 16, so copies of a wave whose rows differ by a multiple of 16 lie
+  // as far apart in the source as in the stage (paired in issue_full).  The
   // source is a per-lane address fixed for the whole loop, advanced by the
   // super-tile's (scalar) offset; only a super-tile that crosses the cache
   // end computes clamped rows (rows past kv_len - 1 re-read row kv_len - 1:
