@@ -276,7 +276,7 @@ int attn_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *
 /*
  * Schedule introspection (host only, no GPU needed).
  *
- * attn_sched_rows writes the query rows per workgroup (128, or 64) and
+ * attn_sched_rows writes the query rows per workgroup (128, 64 or 32) and
  * whether the keys are split between two wave groups (1 or 2) of an
  * attn_fwd / attn_fwd_chunked / attn_fwd_varlen launch of these sizes,
  * causal flag (0/1) and dtype on a device with n_cu compute units (the launch
@@ -286,7 +286,7 @@ int attn_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *
  * 0/1); attn_sched_tile writes which head (b*H + h) and which query rows
  * [row0, row1) workgroup `block` computes.  Every (head, row) is covered by
  * exactly one workgroup; windows run heaviest first.  All return ATTN_OK, or
- * ATTN_E_SHAPE for sizes out of range, rows other than 64 and 128, or a NULL
+ * ATTN_E_SHAPE for sizes out of range, rows other than 32, 64 and 128, or a NULL
  * output pointer (attn_sched_rows: ATTN_E_DTYPE for an unknown dtype).
  */
 int attn_sched_rows(int B, int H, int S_q, int causal, int dtype, int n_cu,

@@ -119,7 +119,7 @@ def test_noncausal_allows_more_queries_than_keys():
     assert call(causal=0, S_q=500, kv_len=7) == A.ATTN_E_DEVICE  # passes validation, stops at the device check
 
 
-@pytest.mark.parametrize("rows", [128, 64])
+@pytest.mark.parametrize("rows", [128, 64, 32])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("B,H,S_q,chunk,kv_len", [
     (1, 1, 1, 1, 1), (1, 1, 128, 128, 128), (1, 1, 129, 129, 129), (2, 3, 300, 64, 300), (2, 4, 300, 100, 300),
@@ -175,7 +175,7 @@ def test_launch_shape_rule():
     16-bit types take 64-row tiles for causal grids below two 128-row tiles
     per CU and for other grids whose last partial round of 128-row tiles
     fills at most half the CUs; fp32 while 64-row tiles still give each
-    workgroup its own CU."""
+    workgroup its own CU.  At most 32 query rows: 32-row tiles, key split."""
     for B, H, S_q in ((1, 1, 1), (1, 1, 128), (8, 8, 512), (4, 8, 512), (4, 8, 513), (4, 8, 2048), (4, 8, 2049),
                       (3, 8, 1024), (8, 8, 768), (5, 8, 1024), (7, 8, 1024), (32, 16, 1024), (16, 16, 98304),
                       (2, 1, 32768), (2, 1, 32769)):
@@ -183,6 +183,9 @@ def test_launch_shape_rule():
         for causal in (False, True):
             for dt in ("f32", "f16", "bf16"):
                 rows, ks = A.sched_rows(B, H, S_q, causal, dt, 256)
+                if S_q <= 32:
+                    assert (rows, ks) == (32, 2)
+                    continue
                 assert ks == (2 if tiles <= 512 else 1)
                 if dt == "f32":
                     fine = 2 * tiles <= 256
@@ -193,6 +196,8 @@ def test_launch_shape_rule():
     assert A.sched_rows(8, 8, 512, False, "f16", 256) == (128, 2)     # c2: one tile per CU
     assert A.sched_rows(8, 8, 512, False, "f32", 256) == (128, 2)
     assert A.sched_rows(1, 1, 128, False, "f32", 256) == (64, 2)      # c1: one tile
+    assert A.sched_rows(32, 16, 1, True, "bf16", 256) == (32, 2)      # a decode step
+    assert A.sched_rows(1, 1, 33, True, "bf16", 256) == (64, 2)
     assert A.sched_rows(4, 8, 1024, True, "bf16", 256) == (64, 2)
     assert A.sched_rows(8, 8, 768, False, "bf16", 256) == (64, 2)     # 384 tiles: 1.5 per CU
     assert A.sched_rows(3, 8, 1024, False, "bf16", 256) == (128, 2)   # 192 tiles: 0.75 per CU
@@ -201,6 +206,8 @@ def test_launch_shape_rule():
         A.sched_rows(1, 1, 1, True, "bf16", 0)
     with pytest.raises(A.AttnError):
         A.sched_grid(1, 1, 128, 128, 128, False, 96)
+    with pytest.raises(A.AttnError):
+        A.sched_grid(1, 1, 128, 128, 128, False, 16)
 
 
 def test_long_context_grid_size():

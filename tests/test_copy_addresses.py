@@ -33,7 +33,7 @@ LANE = np.arange(64)
 
 class Geometry:
     """Compile-time constants of one kernel instance (QG: 32-row query groups
-    per workgroup, 4, or 2 for the 16-bit key split's 64-row tiles)."""
+    per workgroup: 4, or 2 or 1 with the key split's 64- and 32-row tiles)."""
 
     def __init__(self, esz, KS, QG=4):
         self.esz, self.KS, self.QG = esz, KS, QG
@@ -49,7 +49,7 @@ class Geometry:
         self.PG = 1 if (QG * self.RPC) % 16 == 0 else 16 // (QG * self.RPC)
         self.PSTEP = self.PG * self.CSTEP
         assert self.PSTEP in (2048, 4096) and self.NCP % (2 * self.PG) == 0
-        assert QG == 4 or (QG == 2 and KS == 2)
+        assert QG == 4 or (QG in (1, 2) and KS == 2)
         assert QG * KS * 32 * self.ROWB <= self.STAGE   # the Q slabs fit a stage
         sizes = [self.STAGE, self.STAGE, self.STAGE if self.NS == 3 else 16]
         self.stage_base = [0, sizes[0], sizes[0] + sizes[1]]
@@ -70,7 +70,7 @@ class Geometry:
         return 64 * (wave // QG) + self.RPC * (QG * i + wave % QG) + LANE // self.LPR
 
     def wgs_per_cu(self):
-        return 3 if (self.esz == 2 and self.KS == 1) else (2 if (self.QG == 2 and self.esz == 2) else 1)
+        return 3 if (self.esz == 2 and self.KS == 1) else (2 if (self.QG <= 2 and self.esz == 2) else 1)
 
 
 class Box:
@@ -103,15 +103,18 @@ def launch_params(B, H, S_q, S_kv, causal, esz, chunk=None, kv_len=None, n_split
     kv_len = S_kv if kv_len is None else kv_len
     chunk = S_q if chunk is None else chunk
     if n_split > 1:
-        rows, KS = BM, 1
+        rows, KS = (32, 2) if S_q <= 32 else (BM, 1)
     else:
         rows, KS = A.sched_rows(B, H, S_q, causal, "bf16" if esz == 2 else "f32", N_CU)
         tiles = B * H * -(-S_q // BM)
-        if esz == 4:
-            fine = 2 * tiles <= N_CU
+        if S_q <= 32:
+            assert (rows, KS) == (32, 2)
         else:
-            fine = KS == 2 and (tiles < 2 * N_CU if causal else tiles % N_CU != 0 and 2 * (tiles % N_CU) <= N_CU)
-        assert KS == (2 if tiles <= 2 * N_CU else 1) and rows == (64 if fine else 128)
+            if esz == 4:
+                fine = 2 * tiles <= N_CU
+            else:
+                fine = KS == 2 and (tiles < 2 * N_CU if causal else tiles % N_CU != 0 and 2 * (tiles % N_CU) <= N_CU)
+            assert KS == (2 if tiles <= 2 * N_CU else 1) and rows == (64 if fine else 128)
     return dict(B=B, H=H, S_q=S_q, S_kv=S_kv, causal=causal, esz=esz, chunk=chunk, kv_len=kv_len,
                 n_split=n_split, lens=lens, KS=KS, rows=rows, QG=rows // 32)
 

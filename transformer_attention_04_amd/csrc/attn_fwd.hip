@@ -552,11 +552,13 @@ __device__ __forceinline__ void tile32(const char* ks, const char* vs, const flo
 // Occupancy: three four-wave 16-bit workgroups per CU (48 KB of LDS and at
 // most 168 VGPRs each), else one or two.
 template <typename T, bool CAUSAL, int KS, bool VARLEN, bool SPLIT, int QG = 4>
-__global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 : (QG == 2 && sizeof(T) == 2 ? 2 : 1))
+__global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 : (QG <= 2 && sizeof(T) == 2 ? 2 : 1))
     attn_fwd_kernel(Params<T> p) {
-  // QG: 32-row query groups per workgroup (4: 128 rows; 2: 64 rows, key split
-  // only: four waves, two workgroups per CU for 16-bit types, one for fp32).
-  static_assert(QG == 4 || (QG == 2 && KS == 2), "64-row tiles: key split only");
+  // QG: 32-row query groups per workgroup (4: 128 rows; 2: 64 rows; 1: 32
+  // rows, for at most 32 query rows per head: decode steps), the smaller
+  // tiles with the key split only (2 QG waves, two workgroups per CU for
+  // 16-bit types, one for fp32).
+  static_assert(QG == 4 || ((QG == 2 || QG == 1) && KS == 2), "64- and 32-row tiles: key split only");
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ROWB = F32 ? 256 : 128;  // bytes per K/V row (64 elements)
   constexpr int TILE = 64 * ROWB;        // one 64-row tile of K or V
@@ -1280,8 +1282,15 @@ void launch_kernel(const Params<T>& p, int grid, int causal, hipStream_t stream)
 // workgroup a CU of its own (its two LDS stages fill 128 KB): each SIMD then
 // runs one wave instead of two.  The choice depends on B, H, S_q, causal, the
 // type and the CU count only, never on the window size, so chunked and
-// unchunked calls sum in the same order.
+// unchunked calls sum in the same order.  At most 32 query rows per head
+// (decode steps): one 32-row query group per workgroup, its keys split
+// between two waves, so that no wave of the workgroup idles.
 void launch_shape(int B, int H, int S_q, int causal, int dtype, int n_cu, int& rows, int& ks) {
+  if (S_q <= 32) {
+    rows = 32;
+    ks = 2;
+    return;
+  }
   const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
   ks = tiles <= 2 * (int64_t)n_cu ? 2 : 1;
   const int64_t last = tiles % n_cu;  // 128-row tiles in a last, partial round
@@ -1317,27 +1326,31 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   p.c = (float)std::max(std::fabs((double)scale) * 1.4426950408889634, 1e-30);
   p.q_flip = (scale < 0.f) ? (sizeof(T) == 4 ? 0x80000000u : 0x80008000u) : 0u;
   int rows = BM, ks = 1;
-  if (n_split == 1) launch_shape(B, H, S_q, causal, sizeof(T) == 4 ? ATTN_F32 : ATTN_BF16, n_cu, rows, ks);
+  if (n_split == 1) {
+    launch_shape(B, H, S_q, causal, sizeof(T) == 4 ? ATTN_F32 : ATTN_BF16, n_cu, rows, ks);
+  } else if (S_q <= 32) {  // decode steps: 32-row tiles, keys split between two waves in each range
+    rows = 32;
+    ks = 2;
+  }
   p.s = make_sched(B, H, S_q, chunk, kv_len, causal, rows);
   const int grid = p.s.groups * p.s.heads * (p.s.tl + (p.s.n_win - 1) * p.s.tf);
   p.base_grid = grid;
   if (n_split > 1) {
     // Split the keys into n_split ranges of whole 64-key tiles; the four-wave
     // workgroup runs every range (several per CU keep more tile copies in
-    // flight than one eight-wave workgroup).  Ranges past the last tile are
-    // empty.
+    // flight than one eight-wave workgroup), or for at most 32 query rows the
+    // two-wave 32-row workgroup (each wave half of the range).  Ranges past
+    // the last tile are empty.
     const int kv_tiles = (kv_len + BN - 1) / BN;
     const int per = (kv_tiles + n_split - 1) / n_split;
     p.split_span = per * BN;
     p.ws_acc = static_cast<float*>(ws);
     const int64_t rows = (int64_t)B * H * S_q;
     p.ws_ml = p.ws_acc + (int64_t)n_split * rows * HEAD_DIM;
-    if (causal)
-      hipLaunchKernelGGL((attn_fwd_kernel<T, true, 1, false, true>), dim3(grid * n_split), dim3(NTHREADS), 0,
-                         stream, p);
+    if (rows == 32)
+      launch_kernel_v<T, 2, false, true, 1>(p, grid * n_split, causal, stream);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<T, false, 1, false, true>), dim3(grid * n_split), dim3(NTHREADS), 0,
-                         stream, p);
+      launch_kernel_v<T, 1, false, true, 4>(p, grid * n_split, causal, stream);
     if (hipGetLastError() != hipSuccess) return ATTN_E_HIP;
     const int64_t mblocks = (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS;
     hipLaunchKernelGGL((splitkv_merge_kernel<T>), dim3((unsigned)mblocks), dim3(MERGE_THREADS), 0, stream,
@@ -1346,6 +1359,8 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
   }
   if (ks == 1)
     launch_kernel<T, 1>(p, grid, causal, stream);
+  else if (rows == 32)
+    launch_kernel<T, 2, 1>(p, grid, causal, stream);
   else if (rows == 64)
     launch_kernel<T, 2, 2>(p, grid, causal, stream);
   else
@@ -1565,7 +1580,7 @@ extern "C" int attn_sched_rows(int B, int H, int S_q, int causal, int dtype, int
 
 extern "C" int attn_sched_grid(int B, int H, int S_q, int chunk, int kv_len, int causal, int rows, int* grid) {
   if (B < 1 || H < 1 || S_q < 1 || chunk < 1 || kv_len < 1 || !grid) return ATTN_E_SHAPE;
-  if (rows != 64 && rows != BM) return ATTN_E_SHAPE;
+  if (rows != 32 && rows != 64 && rows != BM) return ATTN_E_SHAPE;
   const int64_t bh = (int64_t)B * H;
   const int64_t n_win = ((int64_t)S_q + chunk - 1) / chunk;
   const int64_t tiles = n_win * (((int64_t)std::min(chunk, S_q) + rows - 1) / rows);
