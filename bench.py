@@ -13,7 +13,9 @@ Prints ONE JSON line (rank 0, N = 1):
   cpu_baseline the fp64 oracle on a bounded sample of the same workload, on
                this host's cores
   per_config   the other workloads (c1 .. c4, every dtype), each with its own
-               ms/call, TFLOP/s, roofline and cpu_baseline
+               ms/call, TFLOP/s, roofline and cpu_baseline, and as context
+               library_sdpa: torch's scaled_dot_product_attention (flash or
+               memory-efficient backend) timed on the same inputs
 
 Default workload: the long-context causal chunked workload (B=16, H=16,
 S=98,304, D=64, bf16, 4,096-row query windows against the K/V cache), the
@@ -69,6 +71,9 @@ def parse():
                     help="oracle time per per-config entry's cpu_baseline")
     ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sdpa", action="store_true",
+                    help="skip the per-config library_sdpa context (torch's scaled_dot_product_attention timed "
+                         "on the same inputs)")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--stream", action="store_true",
@@ -527,6 +532,44 @@ def make_sets(w, dtype, dev, log_name=True):
     return sets
 
 
+def library_sdpa(args, w, sets, steps, stream, ours_ms):
+    """Context, not the product: torch's scaled_dot_product_attention (its flash
+    or memory-efficient backend; the math backend is never run) on the same
+    rotating sets, timed like our call, and its largest difference from our
+    output on set 0.  The pages measure their kernel against this library
+    call.  Square workloads only (its causal mask is top-left aligned, which
+    equals the bottom-right one only when S_q = S_kv)."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    if w.S_q != w.S_kv:
+        return None
+    notes = {}
+    for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([be]):
+                def step(i):
+                    q, k, v, _ = sets[i % len(sets)]
+                    F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
+
+                q, k, v, o = sets[0]
+                diff = (F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale).float()
+                        - o.float()).abs().max().item()
+                n = max(len(sets), min(steps, 2000))
+                tm = Timer(step, n, args.repeats, args.eager, stream)
+                total_ms, _ = tm.run()
+                del tm
+        except RuntimeError as ex:  # no kernel of this backend for the dtype or shape
+            notes[be.name] = str(ex).splitlines()[0][:120]
+            continue
+        ms = total_ms / n
+        log(f"[bench] per-config {w.name}: torch SDPA ({be.name}) {ms * 1e3:.2f} us/call, ours "
+            f"{ours_ms * 1e3:.2f} us ({ms / ours_ms:.2f}x)")
+        return {"backend": be.name, "ms_per_call": round(ms, 6), "tflops": round(w.flops() / (ms / 1e3) / 1e12, 4),
+                "steps": n, "ours_speedup": round(ms / ours_ms, 3), "max_abs_diff_vs_ours": diff}
+    return {"unavailable": notes}
+
+
 def per_config_entry(args, name, dtype, dev, stream, peaks):
     """One per-config result: the workload's single call (attn_fwd, or
     attn_fwd_chunked for a chunked workload) over rotating sets, timed like the
@@ -583,7 +626,9 @@ def per_config_entry(args, name, dtype, dev, stream, peaks):
                    "gpu_clock_mhz": clock_block(clk0, clk1)},
     }
     assert e in (2, 4)
-    del tm, sets
+    del tm
+    entry["library_sdpa"] = None if (args.no_sdpa or w.chunk) else library_sdpa(args, w, sets, steps, stream, ms)
+    del sets
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         entry["cpu_baseline"] = cpu_baseline(w, dtype, args.per_config_cpu_seconds)
