@@ -98,10 +98,14 @@ enum attn_status {
  *   dtype      : enum attn_dtype of all four tensors.
  *   stream     : hipStream_t to enqueue on (NULL = null stream).
  * Identical, bit for bit, to attn_fwd_chunked(..., chunk = S_q,
- * kv_len = S_kv).  When B*H*ceil(S_q/128) is at most twice the number of
- * compute units, each 128-row query tile's keys are split between two wave
- * groups and merged at the end (more parallelism for small grids); the split
- * depends on B, H and S_q only.
+ * kv_len = S_kv).  The launch shape follows attn_sched_rows: 128-row query
+ * tiles; when B*H*ceil(S_q/128) is at most twice the number of compute units,
+ * each tile's keys are split between two wave groups (even and odd 64-key
+ * tiles) and merged at the end, and such small grids take 64-row tiles where
+ * 128-row ones would leave compute units idle or unequal, 32-row tiles when
+ * S_q <= 32.  The shape depends on B, H, S_q, causal, dtype and the compute
+ * unit count, never on chunk or kv_len; a row's arithmetic depends only on
+ * whether its keys are split.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o,
              int B, int H, int S_q, int S_kv, int D_h,
@@ -122,8 +126,8 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o,
  * result: each output row is bit-identical to attn_fwd's on the same data.
  * A streaming caller appends a window's K/V rows to the cache and calls with
  * S_q = that window's rows and the grown kv_len; its rows equal the single
- * call's bit for bit when both calls make the same key-split choice (see
- * attn_fwd), and to rounding otherwise.
+ * call's bit for bit when both calls make the same key-split choice
+ * (attn_sched_rows), and to rounding otherwise.
  */
 int attn_fwd_chunked(const void *q, const void *k, const void *v, void *o,
                      int B, int H, int S_q, int S_kv, int D_h,
