@@ -14,12 +14,12 @@
 // Work decomposition (both element types)
 //   workgroup = 4 wavefronts x 32 query rows = BM = 128 rows of one (b, h);
 //   small grids split each tile's keys between two such wave groups (eight
-//   wavefronts), or, for 16-bit types where that leaves CUs unbalanced, take
-//   64-row tiles of 2 query groups x 2 key halves (four wavefronts, two
-//   workgroups per CU); per iteration a wave group stages BN = 64 keys of K
-//   and V in LDS (direct global-to-LDS copies, 16 bytes per lane, into three
-//   stages issued two tiles ahead -- two stages, one ahead, with the key
-//   split);
+//   wavefronts), or, where that leaves CUs unbalanced, take 64-row tiles of
+//   2 query groups x 2 key halves (four wavefronts); calls with at most 32
+//   query rows per head take 32-row tiles of one query group x 2 key halves;
+//   per iteration a wave group stages BN = 64 keys of K and V in LDS (direct
+//   global-to-LDS copies, 16 bytes per lane, into three stages -- two with
+//   the key split);
 //   each wave computes S^T = K Q^T on MFMA so that a lane owns ONE query row
 //   (lane % 32) and 16 keys per 32-key block: the row max and row sum are
 //   in-lane plus one exchange between the two half-waves (v_permlane32_swap);
