@@ -539,6 +539,7 @@ def library_sdpa(args, w, sets, steps, stream, ours_ms):
     output on set 0.  The pages measure their kernel against this library
     call.  Square workloads only (its causal mask is top-left aligned, which
     equals the bottom-right one only when S_q = S_kv)."""
+    import warnings
     import torch
     import torch.nn.functional as F
     from torch.nn.attention import sdpa_kernel, SDPBackend
@@ -547,7 +548,8 @@ def library_sdpa(args, w, sets, steps, stream, ours_ms):
     notes = {}
     for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
         try:
-            with sdpa_kernel([be]):
+            with sdpa_kernel([be]), warnings.catch_warnings():
+                warnings.simplefilter("ignore", UserWarning)  # the backends' notes on unsupported dtypes
                 def step(i):
                     q, k, v, _ = sets[i % len(sets)]
                     F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
