@@ -1071,6 +1071,13 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
   asm volatile("" : "+v"(tx));
   const int ln = tx & 63;
   const int ec = ln & 31, ehf = ln >> 5;
+  // The output rows are stored with the non-temporal hint: this kernel never
+  // reads them back, and streaming them past the caches leaves those to the
+  // K/V tiles other workgroups are still reading.
+  auto store_row = [&](int row, int col, const u32x4& x) __attribute__((always_inline)) {
+    if (wrow0 + row < row1)
+      __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + col));
+  };
   char* ot;
   if constexpr (KS == 1) {
     const int os = (n_super + 1) % 3;
@@ -1100,7 +1107,7 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
     for (int k = 0; k < 8; ++k) {  // rows 4k .. 4k+3
       const int row = 4 * k + ln / 16, ch = ln % 16;
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 256 + 16 * (ch ^ (row & 15)));
-      if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 4 * ch) = x;
+      store_row(row, 4 * ch, x);
     }
   } else {
     typedef Half16<T> H;
@@ -1120,7 +1127,7 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
     for (int k = 0; k < 4; ++k) {  // rows 8k .. 8k+7
       const int row = 8 * k + ln / 8, ch = ln % 8;
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + row * 128 + 16 * (ch ^ (row & 7)));
-      if (wrow0 + row < row1) *reinterpret_cast<u32x4*>(oh + (int64_t)(wrow0 + row) * HEAD_DIM + 8 * ch) = x;
+      store_row(row, 8 * ch, x);
     }
   }
 }

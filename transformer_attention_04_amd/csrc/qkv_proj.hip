@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
     // (selected, not indexed: an indexed kernel-argument array is a memory load)
     T* const ob = which == 0 ? p.out[0] : which == 1 ? p.out[1] : p.out[2];
     T* const orow = ob + (((int64_t)bb * p.H + h) * p.S + sq) * 64;
-    *reinterpret_cast<u32x4*>(orow + 8 * (ch % 8)) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + 8 * (ch % 8)));  // written once, not read here
   }
 }
 
