@@ -221,9 +221,10 @@ int attn_splitkv_workspace_bytes(int B, int H, int S_q, int n_split, size_t *byt
 
 /* A key-range count for attn_fwd_splitkv on a GPU of n_cu compute units: 1
  * when there are at least two 128-row query tiles per CU or the keys span
- * fewer than 16 64-key tiles; otherwise enough ranges for two workgroups per
- * CU, keeping at least 8 key tiles per range.  Host only.  ATTN_E_SHAPE for
- * sizes < 1 or a NULL output. */
+ * fewer than 16 64-key tiles; 2 from one to two tiles per CU; below that
+ * enough ranges for about one workgroup per CU (one per two CUs when there
+ * are fewer than 16 query tiles), keeping at least two key tiles per range.
+ * Host only.  ATTN_E_SHAPE for sizes < 1 or a NULL output. */
 int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, int *n_split);
 
 /*

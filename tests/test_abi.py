@@ -337,11 +337,15 @@ def test_splitkv_workspace_bytes():
     (32, 16, 1024, 1024, 256, 1),      # 4096 query tiles: no split
     (4, 8, 2048, 2048, 256, 1),        # 512 tiles = two per CU
     (16, 16, 1, 98304, 256, 2),        # a decode step of the long cache: 256 tiles -> two ranges
-    (1, 1, 1, 98304, 256, 192),        # one head: 1536 key tiles, at least 8 per range
+    (16, 8, 1, 2048, 256, 2),          # 128 tiles: one workgroup per CU
+    (4, 8, 1, 2048, 256, 8),           # a decode step of 32 heads: 8 ranges, one workgroup per CU
+    (4, 8, 1, 1024, 256, 8),           # 16 key tiles: 8 ranges of two
+    (1, 1, 1, 1024, 256, 8),           # one head, 16 key tiles: ranges keep two key tiles
+    (1, 1, 1, 98304, 256, 128),        # one head (fewer than 16 tiles): one workgroup per two CUs
+    (1, 8, 1, 8192, 256, 16),          # 8 heads: 128 workgroups
+    (2, 4, 16, 4096, 256, 16),         # 8 tiles of 16 rows: 128 workgroups
+    (1, 2, 300, 8192, 256, 22),        # 6 tiles: ceil(128 / 6) ranges
     (1, 1, 128, 128, 256, 1),          # two key tiles: too short to split
-    (2, 4, 16, 4096, 256, 8),          # 8 tiles want 64 ranges; 64 key tiles allow 64 // 8 = 8
-    (1, 2, 300, 8192, 256, 16),        # 6 tiles want 86 ranges; 128 key tiles allow 16
-    (4, 8, 1, 2048, 256, 4),           # a decode step of 32 heads: 32 key tiles allow 4
     (4, 8, 1, 960, 256, 1),            # 15 key tiles: too short to split
 ])
 def test_splitkv_choose(B, H, S_q, kv_len, n_cu, expect):

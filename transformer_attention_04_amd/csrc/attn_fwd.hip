@@ -1136,8 +1136,12 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
 // acc_s and l_s relative to 2^m_s; with M = max m_s the row is
 // O = sum 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s (a range in which the row
 // saw no key has m_s = -inf and weight 0; a row that saw none at all gets
-// zeros).  One thread per row and 16-byte chunk of its 64 columns.
+// zeros).  One thread per row and 16-byte chunk of its 64 columns.  The
+// ranges are read MERGE_BATCH at a time (indices clamped to the last range,
+// the extra copies masked out), so that each batch's loads are in flight
+// together instead of one range's latency after another.
 constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_BATCH = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const float* __restrict__ ws_acc,
@@ -1148,17 +1152,32 @@ __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const floa
   const int64_t row = t >> 4;
   const int ch = (int)(t & 15);
   float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, ws_ml[2 * (s * rows + row)]);
-  float L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < n_split; ++s) {
-    const int64_t pr = s * rows + row;
-    const float m = ws_ml[2 * pr];
-    if (m == -INFINITY) continue;
-    const float w = fast_exp2(m - mx);
-    L += w * ws_ml[2 * pr + 1];
-    const u32x4 x = *reinterpret_cast<const u32x4*>(ws_acc + pr * HEAD_DIM + 4 * ch);
+  for (int s0 = 0; s0 < n_split; s0 += MERGE_BATCH) {
+    float mv[MERGE_BATCH];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] += w * __uint_as_float(x[e]);
+    for (int u = 0; u < MERGE_BATCH; ++u) mv[u] = ws_ml[2 * ((int64_t)min(s0 + u, n_split - 1) * rows + row)];
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) mx = fmaxf(mx, mv[u]);  // repeats of the last range change nothing
+  }
+  float L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += MERGE_BATCH) {
+    u32x2 ml[MERGE_BATCH];
+    u32x4 x[MERGE_BATCH];
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      const int64_t pr = (int64_t)min(s0 + u, n_split - 1) * rows + row;
+      ml[u] = *reinterpret_cast<const u32x2*>(ws_ml + 2 * pr);
+      x[u] = *reinterpret_cast<const u32x4*>(ws_acc + pr * HEAD_DIM + 4 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      const float m = __uint_as_float(ml[u][0]);
+      if (s0 + u >= n_split || m == -INFINITY) continue;
+      const float w = fast_exp2(m - mx);
+      L += w * __uint_as_float(ml[u][1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += w * __uint_as_float(x[u][e]);
+    }
   }
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   if constexpr (sizeof(T) == 4) {
@@ -1502,10 +1521,19 @@ extern "C" int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, 
   if (!n_split || B < 1 || H < 1 || S_q < 1 || kv_len < 1 || n_cu < 1) return ATTN_E_SHAPE;
   const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
   const int64_t kv_tiles = (kv_len + BN - 1) / BN;
+  // Measured on decode steps and short prefill windows: about one workgroup
+  // per CU, or one per two CUs when there are fewer than 16 query tiles (the
+  // merge then reads many ranges per row, and the ranges' chains get short);
+  // two ranges from one to two query tiles per CU.
   int64_t n = 1;
-  if (tiles < 2 * (int64_t)n_cu && kv_tiles >= SPLIT_MIN_KV_TILES) {
-    n = (2 * (int64_t)n_cu + tiles - 1) / tiles;                 // at least two workgroups per CU
-    n = std::min<int64_t>(n, kv_tiles / (SPLIT_MIN_KV_TILES / 2));  // each range keeps a long key chain
+  if (kv_tiles >= SPLIT_MIN_KV_TILES) {
+    if (tiles < n_cu) {
+      const int64_t target = tiles >= 16 ? n_cu : (n_cu + 1) / 2;  // workgroups
+      n = (target + tiles - 1) / tiles;
+      n = std::min<int64_t>(n, kv_tiles / 2);  // each range keeps at least two key tiles
+    } else if (tiles < 2 * (int64_t)n_cu) {
+      n = 2;
+    }
     n = std::max<int64_t>(1, std::min<int64_t>(n, MAX_SPLIT));
   }
   *n_split = (int)n;
