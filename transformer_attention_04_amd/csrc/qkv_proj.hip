@@ -129,24 +129,40 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
   // C[m][n] with m = m0 + 64wm + 32mb + c and n = n0 + 128wn + 32nb +
   // 8(r/4) + 4hf + r%4, so registers 4q .. 4q+3 take 4 consecutive bias
   // values (one 8-byte load; N is a multiple of 64, so n < N covers all 4).
+  // The 16 loads of a lane are issued back to back under one uniform branch
+  // (columns past N read a clamped column and take zero), so they cost one
+  // memory latency rather than sixteen; the first stage's copies are already
+  // in flight.
+  issue(0, 0);
   f32x16 acc[4][2];
+  {
+    u32x2 braw[4][4];
+    if (p.bias) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 128 * wn + 32 * nb + 8 * q + 4 * hf;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.bias && n < p.N) {
-        const u32x2 braw = *reinterpret_cast<const u32x2*>(p.bias + n);
-        const T* bt = reinterpret_cast<const T*>(&braw);
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + 128 * wn + 32 * nb + 8 * q + 4 * hf;
+          braw[nb][q] = *reinterpret_cast<const u32x2*>(p.bias + min(n, p.N - 4));
+        }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = (float)bt[e];
-      }
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[nb][mb][4 * q + e] = bv[e];
+        for (int q = 0; q < 4; ++q) braw[nb][q] = (u32x2){0u, 0u};
     }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 128 * wn + 32 * nb + 8 * q + 4 * hf;
+        const T* bt = reinterpret_cast<const T*>(&braw[nb][q]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[nb][mb][4 * q + e] = n < p.N ? (float)bt[e] : 0.f;
+      }
+  }
 
   // Operand rows 64wm + 32mb + c (x) and 128wn + 32nb + c (W) all have the
   // swizzle sw = (c & 7) ^ ((c >> 3) & 1), so k-step t (chunk 4hf + t, i.e.
@@ -188,7 +204,6 @@ __global__ void __launch_bounds__(PTHREADS, 1) qkv_proj_kernel(ProjParams<T> p) 
   // of kt have landed and every wave is done with kt - 1), compute kt and,
   // inside it, start kt + 1 into kt - 1's buffer.
   const int n_k = p.K / PK;
-  issue(0, 0);
   for (int kt = 0; kt < n_k; ++kt) {
     wait_vmem<0>();
     barrier_keep_dma();
