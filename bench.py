@@ -807,7 +807,9 @@ def main():
         line["per_config"] = [per_config_entry(args, name, dt, dev, stream, peaks) for name, dt in PER_CONFIG]
         line["per_config_note"] = ("each entry times its workload alone for about --per-config-seconds of GPU "
                                    "time (its own step count, 5 repeats, graph replay, rotating sets), "
-                                   "independent of --steps and --warmup, which set the headline's steps")
+                                   "independent of --steps and --warmup, which set the headline's steps; "
+                                   "library_sdpa is context, not this library: torch's scaled_dot_product_attention "
+                                   "(flash or memory-efficient backend) timed the same way on the same inputs")
     emit(args, line)
 
 
