@@ -329,6 +329,21 @@ for b, h, s, lens in VARLEN:
         SHAPES.append(dict(B=b, H=h, S_q=s, S_kv=s, causal=c, lens=lens[:b]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_random_launch_shape_plan_in_bounds(dtype):
+    """Every case of the GPU launch-shape test's plan (all tile heights, key
+    split or not, each entry point with its drawn window, cache length,
+    per-sequence lengths or range count)."""
+    from launch_plan import plan
+    esz = 4 if dtype == "f32" else 2
+    for label, entry, B, H, S_q, S_kv, causal, _, args in plan(dtype, N_CU):
+        kw = {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in args.items()}
+        P = launch_params(B, H, S_q, S_kv, causal, esz, **kw)
+        box = Box(f"{label} entry {entry} {kw}")
+        emulate_current(P, box)
+        assert box.n > 0
+
+
 @pytest.mark.parametrize("esz", [2, 4])
 @pytest.mark.parametrize("n", range(len(SHAPES)))
 def test_every_address_in_bounds(n, esz):
