@@ -164,7 +164,9 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o,
  * Layer" (section "What we learned": running maximum, running sum, rescaled
  * accumulator), and a second kernel merges the ranges' states exactly as the
  * online update merges two blocks: with M the largest offset, O = sum
- * 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s.  This is the regime of few query
+ * 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s (one pass over the ranges, eight
+ * at a time; a batch that raises M first rescales the running sums).  This
+ * is the regime of few query
  * tiles against a long cache (a decode step of the growing cache of the page
  * "Roofline", section "How we built it"; small batches, where the page "GPU
  * Kernel for a Transformer Layer", section "What we learned", loses to a

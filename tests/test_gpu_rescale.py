@@ -77,7 +77,7 @@ def test_forced_rescale_split_keys(dtype):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     for causal in (False, True):
         ref = oracle.attention(q, k, v, causal=causal, scale=SCALE)
-        for n_split in (2, 3, 7):
+        for n_split in (2, 3, 7, 12, 17):  # 12, 17: more ranges than one merge batch (8), so the merge rescales too
             o = A.attn_fwd_splitkv(qd, kd, vd, causal=causal, scale=SCALE, n_split=n_split)
             torch.cuda.synchronize()
             _, ratio = compare(o.float().cpu().numpy(), ref, dtype, f"split {n_split} causal={causal} {dtype}")

@@ -1137,9 +1137,12 @@ __global__ void __launch_bounds__(64 * QG * KS, (sizeof(T) == 2 && KS == 1) ? 3 
 // O = sum 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s (a range in which the row
 // saw no key has m_s = -inf and weight 0; a row that saw none at all gets
 // zeros).  One thread per row and 16-byte chunk of its 64 columns.  The
-// ranges are read MERGE_BATCH at a time (indices clamped to the last range,
-// the extra copies masked out), so that each batch's loads are in flight
-// together instead of one range's latency after another.
+// ranges are read MERGE_BATCH at a time, offsets, sums and accumulators
+// together (indices clamped to the last range, the extra copies masked out),
+// so that a batch costs one memory round trip; M is the largest offset seen
+// so far, and a batch that raises it first rescales the running sums by
+// 2^(M_old - M_new), the online-softmax update at range granularity.  With at
+// most MERGE_BATCH ranges M is the maximum over all of them from the start.
 constexpr int MERGE_THREADS = 256;
 constexpr int MERGE_BATCH = 8;
 
@@ -1151,15 +1154,7 @@ __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const floa
   if (t >= rows * 16) return;
   const int64_t row = t >> 4;
   const int ch = (int)(t & 15);
-  float mx = -INFINITY;
-  for (int s0 = 0; s0 < n_split; s0 += MERGE_BATCH) {
-    float mv[MERGE_BATCH];
-#pragma unroll
-    for (int u = 0; u < MERGE_BATCH; ++u) mv[u] = ws_ml[2 * ((int64_t)min(s0 + u, n_split - 1) * rows + row)];
-#pragma unroll
-    for (int u = 0; u < MERGE_BATCH; ++u) mx = fmaxf(mx, mv[u]);  // repeats of the last range change nothing
-  }
-  float L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+  float mx = -INFINITY, L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < n_split; s0 += MERGE_BATCH) {
     u32x2 ml[MERGE_BATCH];
     u32x4 x[MERGE_BATCH];
@@ -1168,6 +1163,16 @@ __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const floa
       const int64_t pr = (int64_t)min(s0 + u, n_split - 1) * rows + row;
       ml[u] = *reinterpret_cast<const u32x2*>(ws_ml + 2 * pr);
       x[u] = *reinterpret_cast<const u32x4*>(ws_acc + pr * HEAD_DIM + 4 * ch);
+    }
+    float bx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) bx = fmaxf(bx, __uint_as_float(ml[u][0]));  // repeats change nothing
+    if (bx > mx) {  // also the first batch with a visible key; -inf stays -inf
+      const float r = (mx == -INFINITY) ? 0.f : fast_exp2(mx - bx);
+      L *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] *= r;
+      mx = bx;
     }
 #pragma unroll
     for (int u = 0; u < MERGE_BATCH; ++u) {
