@@ -118,3 +118,51 @@ def test_attention_kernels_use_no_dot_instructions(tmp_path):
     assert kernels, "no attention kernel found"
     bad = [(n, ins) for n, b in kernels for ins in _instructions("\n".join(b)) if ins.split()[0].startswith("v_dot")]
     assert not bad, f"{len(bad)} dot instructions in attention kernels, e.g. {bad[0]}"
+
+
+def _kernel_meta(asm):
+    """(name, vgpr, agpr, lds bytes, scratch bytes) of every kernel in the code object metadata."""
+    meta = asm.split("amdhsa.kernels:")[1:]
+    out = []
+    for m in meta:
+        for blk in re.split(r"\n  - ", m)[1:]:
+            def g(k):
+                x = re.search(r"\." + k + r":\s+(\S+)", blk)
+                return x.group(1) if x else None
+            if g("name") is None or g("vgpr_count") is None:
+                continue
+            out.append((g("name"), int(g("vgpr_count")), int(g("agpr_count") or 0),
+                        int(g("group_segment_fixed_size")), int(g("private_segment_fixed_size"))))
+    return out
+
+
+# Workgroups each attention kernel instance must fit per CU: the launch
+# geometry the schedule is built on (16-bit one-group tiles: three four-wave
+# workgroups per CU; the eight-wave key split: one; 64-row key-split tiles:
+# two; the two-wave decode tiles: at least two; fp32: one).  Keyed by
+# (16-bit, KS, QG).
+_WG_PER_CU = {(True, 1, 4): 3, (True, 2, 4): 1, (True, 2, 2): 2, (True, 2, 1): 2,
+              (False, 1, 4): 1, (False, 2, 4): 1, (False, 2, 2): 1, (False, 2, 1): 1}
+
+
+def test_attention_kernels_keep_their_occupancy(tmp_path):
+    # 512 registers (VGPR + AGPR, allocated in granules of 8) per SIMD lane,
+    # four SIMDs and 160 KB of LDS per CU; a kernel that outgrows its
+    # launch bound spills instead, which the scratch limit catches.
+    asm = _device_asm(tmp_path)
+    pat = re.compile(r"attn_fwd_kernelI(DF16b|DF16_|f)Lb[01]ELi(\d)ELb[01]ELb[01]ELi(\d)E")
+    seen = set()
+    for name, vgpr, agpr, lds, scratch in _kernel_meta(asm):
+        m = pat.search(name)
+        if not m:
+            continue
+        key = (m.group(1) != "f", int(m.group(2)), int(m.group(3)))
+        seen.add(key)
+        regs = -(-(-(-vgpr // 4) * 4 + agpr) // 8) * 8
+        waves_per_simd = 512 // regs
+        waves = key[1] * key[2]  # waves per workgroup
+        fit = min(4 * waves_per_simd // waves, (160 * 1024) // lds)
+        assert fit >= _WG_PER_CU[key], (f"{name}: {vgpr} VGPR + {agpr} AGPR, {lds} B LDS fit {fit} workgroups "
+                                         f"per CU, the schedule assumes {_WG_PER_CU[key]}")
+        assert scratch <= 16, f"{name}: {scratch} bytes of scratch per lane (spills)"
+    assert seen == set(_WG_PER_CU), f"kernel instances found: {sorted(seen)}"
