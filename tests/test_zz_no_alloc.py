@@ -21,6 +21,7 @@ CASES = [  # (B, H, S_q, S_kv, kv_len, causal, n_split): the second of each pair
     ((2, 4, 16, 3000, 2900, True, 5), (1, 2, 3, 1000, 1000, False, 3)),     # at most 32 rows: 32-row tiles
     ((4, 8, 1, 4096, 4096, True, 8), (1, 1, 1, 700, 650, True, 2)),
     ((1, 4, 130, 1100, 1100, True, 3), (1, 2, 40, 600, 600, False, 2)),     # 128-row tiles
+    ((1, 2, 1, 8192, 8000, True, 20), (1, 1, 1, 2000, 1999, True, 9)),      # more ranges than one merge batch
 ]
 
 
