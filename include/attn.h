@@ -165,8 +165,9 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o,
  * accumulator), and a second kernel merges the ranges' states exactly as the
  * online update merges two blocks: with M the largest offset, O = sum
  * 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s (one pass over the ranges, eight
- * at a time; a batch that raises M first rescales the running sums).  This
- * is the regime of few query
+ * at a time; a batch that raises M first rescales the running sums; beyond
+ * 24 ranges sixteen threads share each row's ranges and combine their sums
+ * the same way).  This is the regime of few query
  * tiles against a long cache (a decode step of the growing cache of the page
  * "Roofline", section "How we built it"; small batches, where the page "GPU
  * Kernel for a Transformer Layer", section "What we learned", loses to a
@@ -224,8 +225,8 @@ int attn_splitkv_workspace_bytes(int B, int H, int S_q, int n_split, size_t *byt
 /* A key-range count for attn_fwd_splitkv on a GPU of n_cu compute units: 1
  * when there are at least two 128-row query tiles per CU or the keys span
  * fewer than 16 64-key tiles; 2 from one to two tiles per CU; below that
- * enough ranges for about one workgroup per CU (one per two CUs when there
- * are fewer than 16 query tiles), keeping at least two key tiles per range.
+ * enough ranges for about one workgroup per CU, keeping at least two key
+ * tiles per range.
  * Host only.  ATTN_E_SHAPE for sizes < 1 or a NULL output. */
 int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, int *n_split);
 

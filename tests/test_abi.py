@@ -341,10 +341,11 @@ def test_splitkv_workspace_bytes():
     (4, 8, 1, 2048, 256, 8),           # a decode step of 32 heads: 8 ranges, one workgroup per CU
     (4, 8, 1, 1024, 256, 8),           # 16 key tiles: 8 ranges of two
     (1, 1, 1, 1024, 256, 8),           # one head, 16 key tiles: ranges keep two key tiles
-    (1, 1, 1, 98304, 256, 128),        # one head (fewer than 16 tiles): one workgroup per two CUs
-    (1, 8, 1, 8192, 256, 16),          # 8 heads: 128 workgroups
-    (2, 4, 16, 4096, 256, 16),         # 8 tiles of 16 rows: 128 workgroups
-    (1, 2, 300, 8192, 256, 22),        # 6 tiles: ceil(128 / 6) ranges
+    (1, 1, 1, 98304, 256, 256),        # one head: one range per CU (the ranges merge in parallel)
+    (1, 8, 1, 8192, 256, 32),          # 8 heads: 256 workgroups
+    (2, 4, 16, 4096, 256, 32),         # 8 tiles of 16 rows: 256 workgroups
+    (1, 2, 300, 8192, 256, 43),        # 6 tiles: ceil(256 / 6) ranges
+    (1, 1, 1, 16384, 256, 128),        # 256 key tiles: ranges keep two
     (1, 1, 128, 128, 256, 1),          # two key tiles: too short to split
     (4, 8, 1, 960, 256, 1),            # 15 key tiles: too short to split
 ])

@@ -45,6 +45,7 @@ CASES = [
     (1, 1, 128, 128, 128, False, (2,)),                   # the single-head 128 x 128 shape
     (2, 2, 200, 3000, 2900, True, (3, 6)),                # two query tiles, a ragged one
     (1, 4, 16, 1030, 1030, False, (5,)),
+    (1, 2, 100, 6000, 5900, True, (30, 47)),              # more than three merge batches: the row-parallel merge
 ]
 
 

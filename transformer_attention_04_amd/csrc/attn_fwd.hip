@@ -1195,6 +1195,87 @@ __global__ void __launch_bounds__(MERGE_THREADS) splitkv_merge_kernel(const floa
   }
 }
 
+// The merge for more ranges than three batches: one workgroup per row,
+// sixteen range groups x sixteen 16-byte chunks.  Group g folds ranges g, g + 16,
+// g + 32, ... (MERGE_BATCH per memory round trip, the same running update as
+// above), so up to 128 ranges take one round trip instead of one per batch;
+// then the sixteen groups' (M_g, L_g, acc_g) of each chunk are combined
+// through LDS with weights 2^(M_g - M).  Same result as the one-thread merge
+// up to fp32 summation order.
+constexpr int MERGE_GROUPS = 16;
+
+template <typename T>
+__global__ void __launch_bounds__(MERGE_GROUPS * 16) splitkv_merge_rows_kernel(const float* __restrict__ ws_acc,
+                                                                              const float* __restrict__ ws_ml,
+                                                                              T* __restrict__ o, int64_t rows,
+                                                                              int n_split) {
+  const int64_t row = blockIdx.x;
+  const int ch = threadIdx.x & 15, g = threadIdx.x >> 4;
+  float mx = -INFINITY, L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = g; s0 < n_split; s0 += MERGE_GROUPS * MERGE_BATCH) {
+    u32x2 ml[MERGE_BATCH];
+    u32x4 x[MERGE_BATCH];
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      const int sr = s0 + MERGE_GROUPS * u;
+      const int64_t pr = (int64_t)(sr < n_split ? sr : g) * rows + row;  // g < n_split: a valid range
+      ml[u] = *reinterpret_cast<const u32x2*>(ws_ml + 2 * pr);
+      x[u] = *reinterpret_cast<const u32x4*>(ws_acc + pr * HEAD_DIM + 4 * ch);
+    }
+    float bx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u)
+      if (s0 + MERGE_GROUPS * u < n_split) bx = fmaxf(bx, __uint_as_float(ml[u][0]));
+    if (bx > mx) {
+      const float r = (mx == -INFINITY) ? 0.f : fast_exp2(mx - bx);
+      L *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] *= r;
+      mx = bx;
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      const float m = __uint_as_float(ml[u][0]);
+      if (s0 + MERGE_GROUPS * u >= n_split || m == -INFINITY) continue;
+      const float w = fast_exp2(m - mx);
+      L += w * __uint_as_float(ml[u][1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += w * __uint_as_float(x[u][e]);
+    }
+  }
+  __shared__ float part[MERGE_GROUPS][16][6];
+  part[g][ch][0] = mx;
+  part[g][ch][1] = L;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) part[g][ch][2 + e] = a[e];
+  __syncthreads();
+  if (g != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < MERGE_GROUPS; ++h) M = fmaxf(M, part[h][ch][0]);
+  L = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < MERGE_GROUPS; ++h) {
+    const float mh = part[h][ch][0];
+    if (mh == -INFINITY) continue;  // a group with no visible key (or no range)
+    const float w = fast_exp2(mh - M);
+    L += w * part[h][ch][1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += w * part[h][ch][2 + e];
+  }
+  const float inv = (L > 0.f) ? 1.0f / L : 0.f;
+  if constexpr (sizeof(T) == 4) {
+    const u32x4 w = {__float_as_uint(a[0] * inv), __float_as_uint(a[1] * inv), __float_as_uint(a[2] * inv),
+                     __float_as_uint(a[3] * inv)};
+    *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(o) + row * HEAD_DIM + 4 * ch) = w;
+  } else {
+    const u32x2 w = {Half16<T>::pack2(a[0] * inv, a[1] * inv), Half16<T>::pack2(a[2] * inv, a[3] * inv)};
+    *reinterpret_cast<u32x2*>(o + row * HEAD_DIM + 4 * ch) = w;
+  }
+}
+
 }  // namespace
 
 // The split-key partial states of attn_fwd_splitkv_noalloc: device memory of
@@ -1383,9 +1464,14 @@ int launch_typed(const void* q, const void* k, const void* v, void* o, int B, in
     else
       launch_kernel_v<T, 1, false, true, 4>(p, grid * n_split, causal, stream);
     if (hipGetLastError() != hipSuccess) return ATTN_E_HIP;
-    const int64_t mblocks = (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS;
-    hipLaunchKernelGGL((splitkv_merge_kernel<T>), dim3((unsigned)mblocks), dim3(MERGE_THREADS), 0, stream,
-                       p.ws_acc, p.ws_ml, static_cast<T*>(o), rows, n_split);
+    if (n_split > 3 * MERGE_BATCH && rows <= (int64_t)INT32_MAX) {  // more than three batches per row
+      hipLaunchKernelGGL((splitkv_merge_rows_kernel<T>), dim3((unsigned)rows), dim3(MERGE_GROUPS * 16), 0, stream,
+                         p.ws_acc, p.ws_ml, static_cast<T*>(o), rows, n_split);
+    } else {
+      const int64_t mblocks = (rows * 16 + MERGE_THREADS - 1) / MERGE_THREADS;
+      hipLaunchKernelGGL((splitkv_merge_kernel<T>), dim3((unsigned)mblocks), dim3(MERGE_THREADS), 0, stream,
+                         p.ws_acc, p.ws_ml, static_cast<T*>(o), rows, n_split);
+    }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_HIP;
   }
   if (ks == 1)
@@ -1527,14 +1613,13 @@ extern "C" int attn_splitkv_choose(int B, int H, int S_q, int kv_len, int n_cu, 
   const int64_t tiles = (int64_t)B * H * ((S_q + BM - 1) / BM);
   const int64_t kv_tiles = (kv_len + BN - 1) / BN;
   // Measured on decode steps and short prefill windows: about one workgroup
-  // per CU, or one per two CUs when there are fewer than 16 query tiles (the
-  // merge then reads many ranges per row, and the ranges' chains get short);
-  // two ranges from one to two query tiles per CU.
+  // per CU (rows with many ranges merge them in parallel, so a single head
+  // against a long cache takes as many ranges as there are CUs); two ranges
+  // from one to two query tiles per CU.
   int64_t n = 1;
   if (kv_tiles >= SPLIT_MIN_KV_TILES) {
     if (tiles < n_cu) {
-      const int64_t target = tiles >= 16 ? n_cu : (n_cu + 1) / 2;  // workgroups
-      n = (target + tiles - 1) / tiles;
+      n = (n_cu + tiles - 1) / tiles;  // about n_cu workgroups
       n = std::min<int64_t>(n, kv_tiles / 2);  // each range keeps at least two key tiles
     } else if (tiles < 2 * (int64_t)n_cu) {
       n = 2;
