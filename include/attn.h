@@ -166,8 +166,8 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o,
  * online update merges two blocks: with M the largest offset, O = sum
  * 2^(m_s - M) acc_s / sum 2^(m_s - M) l_s (one pass over the ranges, eight
  * at a time; a batch that raises M first rescales the running sums; beyond
- * 24 ranges sixteen threads share each row's ranges and combine their sums
- * the same way).  This is the regime of few query
+ * 24 ranges each row's ranges are dealt to sixteen groups of threads whose
+ * sums are then combined the same way).  This is the regime of few query
  * tiles against a long cache (a decode step of the growing cache of the page
  * "Roofline", section "How we built it"; small batches, where the page "GPU
  * Kernel for a Transformer Layer", section "What we learned", loses to a
