@@ -52,7 +52,10 @@ def plan(dtype, n_cu=256):
             elif entry == 2:
                 args = dict(lens=rng.randint(0, S_kv + 4, size=B).astype(np.int32))
             elif entry == 3:
-                n_split = int(rng.randint(1, 7))
+                # few ranges (one merge thread per row and chunk), or, for small row counts, more than 24
+                # (the merge that deals each row's ranges to sixteen thread groups)
+                many = B * H * S_q <= 4096 and rng.rand() < 0.5
+                n_split = int(rng.randint(25, 65)) if many else int(rng.randint(1, 7))
                 args = dict(n_split=n_split, kv_len=int(rng.randint(lo, S_kv + 1)))
             else:
                 args = {}
